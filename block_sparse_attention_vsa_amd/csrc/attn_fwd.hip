@@ -1,0 +1,358 @@
+// Block-sparse attention forward on gfx950.
+//
+// What is computed (machinebrief LVSA article: block-sparse attention; Sparse
+// VideoGen2 page, Abstract: compute only the critical tokens; OSP-Next page,
+// "Method": sparse attention kept FlashAttention-compatible): for each (b, h)
+// and query i, O_i = sum_j softmax_j(scale <q_i, k_j>) v_j over the valid keys j
+// of the key blocks kept for i's query block. Masked tiles are never loaded.
+//
+// bf16 kernel, one workgroup per (b, h, query block of BS rows), BS/32 waves:
+//  * each wave owns 32 query rows; Q stays in registers for the whole loop;
+//  * for every kept key block the workgroup stages K (row-major) and V
+//    (transposed, keys contiguous per channel) in LDS with XOR-swizzled 16-byte
+//    chunks, so every 8-lane group of a ds_read_b128 touches distinct banks;
+//  * S^T = K Q^T on v_mfma_f32_32x32x16_bf16: the accumulator gives each lane one
+//    query and 16 keys per 32-key sub-tile, so a query's row max and row sum are
+//    lane-local except for one exchange between the two half-waves;
+//  * online softmax in fp32 in the log2 domain (scale * log2 e folded into one
+//    FMA before v_exp_f32), P rounded to bf16;
+//  * O^T += V^T P^T on the same MFMA with P taken straight from the score
+//    registers: the transposed-V chunk order in LDS matches the order in which
+//    the accumulator holds the keys (bits 2 and 3 of the key index swapped).
+//  * The grid is remapped so that consecutive query blocks of a head run on the
+//    same XCD (workgroups are dealt round-robin over the 8 XCDs), which keeps
+//    the overlapping key windows of neighbouring query blocks in that XCD's L2.
+#include <math.h>
+
+#include "mfma_tile.h"
+
+namespace vsa {
+
+constexpr int kMaxMaskBlocks = 4096;   // key blocks a mask row may hold (mask form)
+
+struct AttnArgs {
+    const uint16_t* q;
+    const uint16_t* k;
+    const uint16_t* v;
+    uint16_t* o;
+    float* lse;
+    const int32_t* blk_len;
+    const uint8_t* mask;
+    const int32_t* kv_idx;
+    const int32_t* kv_cnt;
+    int32_t max_kv;
+    int32_t H, N, nb;
+    int32_t num_items;
+    float scale_log2;      // scale * log2(e)
+};
+
+__device__ __forceinline__ int xcd_remap(int bid, int G) {
+    // Workgroup `bid` runs on XCD bid % 8; give each XCD a contiguous item range.
+    int x = bid & 7, j = bid >> 3;
+    int q = G >> 3, r = G & 7;
+    return x * q + min(x, r) + j;
+}
+
+__device__ __forceinline__ int block_valid(const int32_t* blk_len, int b, int BS, int N) {
+    int exist = min(BS, N - b * BS);
+    return blk_len ? min(blk_len[b], exist) : exist;
+}
+
+// Builds this workgroup's ascending list of kept key blocks from a mask row.
+template <int THREADS>
+__device__ int compact_mask_row(const uint8_t* row, int nkb, int16_t* list, int* wave_cnt) {
+    constexpr int WAVES = THREADS / 64;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    int base = 0;
+    for (int r0 = 0; r0 < nkb; r0 += THREADS) {
+        int e = r0 + threadIdx.x;
+        bool keep = e < nkb && row[e] != 0;
+        uint64_t bal = __ballot(keep);
+        if (lane == 0) wave_cnt[w] = __popcll(bal);
+        __syncthreads();
+        int before = 0, total = 0;
+#pragma unroll
+        for (int i = 0; i < WAVES; ++i) {
+            int c = wave_cnt[i];
+            before += (i < w) ? c : 0;
+            total += c;
+        }
+        if (keep) list[base + before + __popcll(bal & ((1ull << lane) - 1ull))] = (int16_t)e;
+        base += total;
+        __syncthreads();
+    }
+    return base;
+}
+
+template <int D, int BS>
+__global__ __launch_bounds__(BS * 2) void attn_fwd_bf16_kernel(AttnArgs a) {
+    constexpr int WAVES = BS / 32;
+    constexpr int THREADS = WAVES * 64;
+    constexpr int NST = BS / 32;               // 32-key sub-tiles per key block
+    constexpr int NDT = D / 32;                // 32-channel tiles of O
+
+    __shared__ __attribute__((aligned(16))) uint8_t k_lds[BS * D * 2];
+    __shared__ __attribute__((aligned(16))) uint8_t v_lds[D * BS * 2];
+    __shared__ int16_t list_lds[kMaxMaskBlocks];
+    __shared__ int wave_cnt[WAVES];
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int l32 = lane & 31, half = lane >> 5;
+    const int nqb = a.nb, nkb = a.nb;
+    const int item = xcd_remap(blockIdx.x, a.num_items);
+    const int bh = item / nqb, qb = item - bh * nqb;
+    const int64_t head_off = (int64_t)bh * a.N * D;
+    const int valid_q = block_valid(a.blk_len, qb, BS, a.N);
+    const bool wave_active = 32 * w < valid_q;
+
+    // ---- kept key blocks -------------------------------------------------
+    int cnt;
+    const int32_t* list_g = nullptr;
+    if (a.mask) {
+        cnt = compact_mask_row<THREADS>(a.mask + (int64_t)item * nkb, nkb, list_lds, wave_cnt);
+    } else {
+        cnt = min(a.kv_cnt[item], a.max_kv);
+        list_g = a.kv_idx + (int64_t)item * a.max_kv;
+    }
+
+    // ---- Q fragment (registers for the whole loop) -------------------------
+    const int q_local = 32 * w + l32;
+    const int q_row = qb * BS + q_local;
+    const bool q_ok = q_local < valid_q;
+    bf16x8 qf[D / 16];
+    load_q_frag<D>(qf, a.q + head_off + (int64_t)q_row * D, q_ok, half);
+
+    f32x16 o_acc[NDT];
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) o_acc[dt] = f32x16{};
+    float m_run = -INFINITY, l_run = 0.f;
+
+    for (int it = 0; it < cnt; ++it) {
+        const int kb = a.mask ? (int)list_lds[it] : list_g[it];
+        if ((unsigned)kb >= (unsigned)nkb) continue;           // malformed entry: skip
+        const int valid_k = block_valid(a.blk_len, kb, BS, a.N);
+        const int64_t key0 = head_off + (int64_t)kb * BS * D;
+
+        __syncthreads();   // previous tile fully consumed
+        stage_k_tile<D, BS, THREADS>(k_lds, a.k + key0, valid_k, tid);
+        stage_v_tile<D, BS, THREADS>(v_lds, a.v + key0, valid_k, tid);
+        __syncthreads();
+
+        if (wave_active) {
+            f32x16 s[NST];
+            tile_scores<D, BS>(s, k_lds, qf, l32, half);
+            if (valid_k < BS) {                                   // keys past the block's valid length
+#pragma unroll
+                for (int st = 0; st < NST; ++st)
+#pragma unroll
+                    for (int x = 0; x < 16; ++x)
+                        if (acc_key(st, x, half) >= valid_k) s[st][x] = -INFINITY;
+            }
+            // ---- online softmax (log2 domain) ---------------------------------
+            float mx = -INFINITY;
+#pragma unroll
+            for (int st = 0; st < NST; ++st)
+#pragma unroll
+                for (int x = 0; x < 16; ++x) mx = fmaxf(mx, s[st][x]);
+            mx = fmaxf(mx, swap_halves(mx));
+            const float m_new = fmaxf(m_run, mx * a.scale_log2);
+            const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+            const float alpha = exp2f(m_run - m_use);
+            float psum = 0.f;
+            bf16x8 pf[NST][2];
+#pragma unroll
+            for (int st = 0; st < NST; ++st) {
+#pragma unroll
+                for (int x = 0; x < 16; ++x) {
+                    float p = exp2f(fmaf(s[st][x], a.scale_log2, -m_use));
+                    psum += p;
+                    pf[st][x >> 3][x & 7] = (__bf16)p;
+                }
+            }
+            l_run = l_run * alpha + psum;
+            m_run = m_new;
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+                for (int x = 0; x < 16; ++x) o_acc[dt][x] *= alpha;
+            tile_pv<D, BS>(o_acc, v_lds, pf, l32, half);
+        }
+    }
+
+    // ---- epilogue ----------------------------------------------------------
+    const float l_tot = l_run + swap_halves(l_run);
+    if (q_row < a.N) {
+        const bool has = q_ok && l_tot > 0.f;
+        const float inv = has ? 1.f / l_tot : 0.f;
+        uint16_t* orow = a.o + head_off + (int64_t)q_row * D;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                __bf16 b0 = (__bf16)(o_acc[dt][4 * j + 0] * inv);
+                __bf16 b1 = (__bf16)(o_acc[dt][4 * j + 1] * inv);
+                __bf16 b2 = (__bf16)(o_acc[dt][4 * j + 2] * inv);
+                __bf16 b3 = (__bf16)(o_acc[dt][4 * j + 3] * inv);
+                u32x2 pk;
+                pk.x = (uint32_t)__builtin_bit_cast(uint16_t, b0) | ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16);
+                pk.y = (uint32_t)__builtin_bit_cast(uint16_t, b2) | ((uint32_t)__builtin_bit_cast(uint16_t, b3) << 16);
+                *reinterpret_cast<u32x2*>(orow + 32 * dt + 8 * j + 4 * half) = pk;
+            }
+        if (a.lse && half == 0)
+            a.lse[(int64_t)bh * a.N + q_row] = has ? (m_run + log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
+    }
+}
+
+// fp32 kernel (block size 64): one thread per query row, K and V tiles in LDS,
+// exact fp32 arithmetic with an online softmax per tile.
+template <int D>
+__global__ __launch_bounds__(64) void attn_fwd_f32_kernel(AttnArgs a) {
+    constexpr int BS = 64;
+    __shared__ __attribute__((aligned(16))) float k_lds[BS * D];
+    __shared__ __attribute__((aligned(16))) float v_lds[BS * D];
+    __shared__ int16_t list_lds[kMaxMaskBlocks];
+    __shared__ int wave_cnt[1];
+    const float* Q = reinterpret_cast<const float*>(a.q);
+    const float* K = reinterpret_cast<const float*>(a.k);
+    const float* V = reinterpret_cast<const float*>(a.v);
+    float* O = reinterpret_cast<float*>(a.o);
+    const int tid = threadIdx.x;
+    const int nkb = a.nb;
+    const int item = xcd_remap(blockIdx.x, a.num_items);
+    const int bh = item / a.nb, qb = item - bh * a.nb;
+    const int64_t head_off = (int64_t)bh * a.N * D;
+    const int valid_q = block_valid(a.blk_len, qb, BS, a.N);
+    int cnt;
+    const int32_t* list_g = nullptr;
+    if (a.mask) {
+        cnt = compact_mask_row<64>(a.mask + (int64_t)item * nkb, nkb, list_lds, wave_cnt);
+    } else {
+        cnt = min(a.kv_cnt[item], a.max_kv);
+        list_g = a.kv_idx + (int64_t)item * a.max_kv;
+    }
+    const int q_row = qb * BS + tid;
+    const bool q_ok = tid < valid_q;
+    float qv[D], ov[D];
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+        qv[d] = q_ok ? Q[head_off + (int64_t)q_row * D + d] : 0.f;
+        ov[d] = 0.f;
+    }
+    float m_run = -INFINITY, l_run = 0.f;
+    for (int it = 0; it < cnt; ++it) {
+        const int kb = a.mask ? (int)list_lds[it] : list_g[it];
+        if ((unsigned)kb >= (unsigned)nkb) continue;
+        const int valid_k = block_valid(a.blk_len, kb, BS, a.N);
+        const int64_t key0 = head_off + (int64_t)kb * BS * D;
+        __syncthreads();
+        for (int i = tid; i < BS * D / 4; i += 64) {
+            int r = (4 * i) / D;
+            f32x4 kt = {0.f, 0.f, 0.f, 0.f}, vt = {0.f, 0.f, 0.f, 0.f};
+            if (r < valid_k) {
+                kt = *reinterpret_cast<const f32x4*>(K + key0 + 4 * i);
+                vt = *reinterpret_cast<const f32x4*>(V + key0 + 4 * i);
+            }
+            *reinterpret_cast<f32x4*>(k_lds + 4 * i) = kt;
+            *reinterpret_cast<f32x4*>(v_lds + 4 * i) = vt;
+        }
+        __syncthreads();
+        float s[BS];
+        float mx = -INFINITY;
+        for (int j = 0; j < BS; ++j) {
+            float acc = 0.f;
+#pragma unroll
+            for (int d = 0; d < D; ++d) acc = fmaf(qv[d], k_lds[j * D + d], acc);
+            s[j] = (j < valid_k) ? acc * a.scale_log2 : -INFINITY;
+            mx = fmaxf(mx, s[j]);
+        }
+        const float m_new = fmaxf(m_run, mx);
+        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+        const float alpha = exp2f(m_run - m_use);
+        l_run *= alpha;
+#pragma unroll
+        for (int d = 0; d < D; ++d) ov[d] *= alpha;
+        for (int j = 0; j < BS; ++j) {
+            float p = exp2f(s[j] - m_use);
+            l_run += p;
+#pragma unroll
+            for (int d = 0; d < D; ++d) ov[d] = fmaf(p, v_lds[j * D + d], ov[d]);
+        }
+        m_run = m_new;
+    }
+    if (q_row < a.N) {
+        const bool has = q_ok && l_run > 0.f;
+        const float inv = has ? 1.f / l_run : 0.f;
+#pragma unroll
+        for (int d = 0; d < D; ++d) O[head_off + (int64_t)q_row * D + d] = ov[d] * inv;
+        if (a.lse) a.lse[(int64_t)bh * a.N + q_row] = has ? (m_run + log2f(l_run)) * 0.69314718055994531f : -INFINITY;
+    }
+}
+
+}  // namespace vsa
+
+using namespace vsa;
+
+extern "C" size_t vsa_attn_workspace_bytes(int B, int H, int N, int bs, int max_kv) {
+    (void)B; (void)H; (void)N; (void)bs; (void)max_kv;
+    return 0;
+}
+
+extern "C" int vsa_block_sparse_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                                         int H, int N, int D, int dtype, int bs, const int32_t* blk_len,
+                                         const vsa_blocks* blocks, float scale, void* workspace, size_t ws_bytes,
+                                         void* stream) {
+    (void)workspace; (void)ws_bytes;
+    if (!q || !k || !v || !o) return fail(VSA_ERR_INVALID, "vsa_block_sparse_attn_fwd: null tensor");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+        return fail(VSA_ERR_INVALID, "vsa_block_sparse_attn_fwd: tensors must be 16-byte aligned");
+    if (B <= 0 || H <= 0 || N <= 0) return fail(VSA_ERR_INVALID, "vsa_block_sparse_attn_fwd: B, H, N must be positive");
+    if (!blocks) return fail(VSA_ERR_INVALID, "vsa_block_sparse_attn_fwd: null blocks");
+    const bool has_mask = blocks->mask != nullptr;
+    const bool has_list = blocks->kv_idx != nullptr || blocks->kv_cnt != nullptr;
+    if (has_mask == has_list)
+        return fail(VSA_ERR_INVALID, "vsa_block_sparse_attn_fwd: give exactly one of mask or (kv_idx, kv_cnt)");
+    if (has_list && (!blocks->kv_idx || !blocks->kv_cnt || blocks->max_kv <= 0))
+        return fail(VSA_ERR_INVALID, "vsa_block_sparse_attn_fwd: list form needs kv_idx, kv_cnt and max_kv > 0");
+    if (!(scale > 0.f) || !__builtin_isfinite(scale))
+        return fail(VSA_ERR_INVALID, "vsa_block_sparse_attn_fwd: scale must be positive and finite");
+    if (D != 64 && D != 128) return fail(VSA_ERR_UNSUPPORTED, "vsa_block_sparse_attn_fwd: D must be 64 or 128 (got %d)", D);
+    if (dtype == VSA_BF16) {
+        if (bs != 64 && bs != 128) return fail(VSA_ERR_UNSUPPORTED, "vsa_block_sparse_attn_fwd: bf16 needs bs 64 or 128 (got %d)", bs);
+    } else if (dtype == VSA_F32) {
+        if (bs != 64) return fail(VSA_ERR_UNSUPPORTED, "vsa_block_sparse_attn_fwd: fp32 needs bs 64 (got %d)", bs);
+    } else {
+        return fail(VSA_ERR_UNSUPPORTED, "vsa_block_sparse_attn_fwd: dtype %d not supported", dtype);
+    }
+    const int64_t nb = (N + (int64_t)bs - 1) / bs;
+    if (has_mask && nb > kMaxMaskBlocks)
+        return fail(VSA_ERR_UNSUPPORTED, "vsa_block_sparse_attn_fwd: mask form supports at most %d blocks per row (use the list form)", kMaxMaskBlocks);
+    const int64_t items = (int64_t)B * H * nb;
+    if (items >= (1ll << 31) || (int64_t)B * H * N * D >= (1ll << 40))
+        return fail(VSA_ERR_INVALID, "vsa_block_sparse_attn_fwd: problem too large");
+    AttnArgs a;
+    a.q = static_cast<const uint16_t*>(q);
+    a.k = static_cast<const uint16_t*>(k);
+    a.v = static_cast<const uint16_t*>(v);
+    a.o = static_cast<uint16_t*>(o);
+    a.lse = lse;
+    a.blk_len = blk_len;
+    a.mask = blocks->mask;
+    a.kv_idx = blocks->kv_idx;
+    a.kv_cnt = blocks->kv_cnt;
+    a.max_kv = has_list ? blocks->max_kv : 0;
+    a.H = H; a.N = N; a.nb = (int32_t)nb;
+    a.num_items = (int32_t)items;
+    a.scale_log2 = (float)((double)scale * 1.4426950408889634);
+    hipStream_t s = as_stream(stream);
+    dim3 grid((unsigned)items);
+    if (dtype == VSA_BF16) {
+        if (D == 128 && bs == 128) hipLaunchKernelGGL((attn_fwd_bf16_kernel<128, 128>), grid, dim3(256), 0, s, a);
+        else if (D == 128 && bs == 64) hipLaunchKernelGGL((attn_fwd_bf16_kernel<128, 64>), grid, dim3(128), 0, s, a);
+        else if (D == 64 && bs == 128) hipLaunchKernelGGL((attn_fwd_bf16_kernel<64, 128>), grid, dim3(256), 0, s, a);
+        else hipLaunchKernelGGL((attn_fwd_bf16_kernel<64, 64>), grid, dim3(128), 0, s, a);
+    } else {
+        if (D == 64) hipLaunchKernelGGL((attn_fwd_f32_kernel<64>), grid, dim3(64), 0, s, a);
+        else hipLaunchKernelGGL((attn_fwd_f32_kernel<128>), grid, dim3(64), 0, s, a);
+    }
+    return launch_status("vsa_block_sparse_attn_fwd");
+}

@@ -1,0 +1,144 @@
+// Device building blocks shared by the attention and profiler kernels: LDS
+// staging of a key/value tile and the two MFMA products of one tile.
+//
+// Layouts (KT keys per tile, D channels, bf16):
+//  * K tile, row-major [KT][D]: the 16-byte chunk c of key r is stored at chunk
+//    c ^ (r & 7) of its row, so the 8 lanes of a ds_read_b128 group (8
+//    consecutive keys, same chunk) hit 8 distinct bank groups.
+//  * V tile, transposed [D][KT]: row d holds the tile's keys; key kappa is stored
+//    at position pos(kappa) = kappa with bits 2 and 3 swapped, and 16-byte chunk
+//    x of row d at chunk x ^ ((d ^ d >> 3) & 7).
+//  * S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (A = 32 keys x 16 channels from
+//    LDS, B = 16 channels x 32 queries from registers). Accumulator element x of
+//    sub-tile st in lane l holds key 32 st + 8 (x >> 2) + 4 (l >> 5) + (x & 3) of
+//    query l & 31.
+//  * O^T += V^T P^T: the B operand for keys [32 st + 16 g, +16) is accumulator
+//    elements [8 g, 8 g + 8) of sub-tile st converted to bf16; the A operand slot
+//    (half h, element e) then needs key 32 st + 16 g + 8 (e >> 2) + 4 h + (e & 3),
+//    whose transposed position 32 st + 16 g + 8 h + e makes the 8 values of a
+//    lane one contiguous 16-byte chunk.
+#pragma once
+
+#include "vsa_internal.h"
+
+namespace vsa {
+
+template <int D, int KT>
+__device__ __forceinline__ int k_lds_off(int r, int c) {
+    return r * D * 2 + ((c ^ (r & 7)) << 4);
+}
+
+template <int D, int KT>
+__device__ __forceinline__ int v_lds_off(int d, int chunk) {
+    return d * KT * 2 + ((chunk ^ ((d ^ (d >> 3)) & 7)) << 4);
+}
+
+// Stage a K tile: rows [0, valid) from global (row stride D), zeros after.
+template <int D, int KT, int THREADS>
+__device__ __forceinline__ void stage_k_tile(uint8_t* k_lds, const uint16_t* kg, int valid, int tid) {
+    constexpr int KCH = D / 8;
+    static_assert((KT * KCH) % THREADS == 0, "K tile must split evenly over the threads");
+#pragma unroll
+    for (int u = 0; u < KT * KCH / THREADS; ++u) {
+        int i = tid + THREADS * u;
+        int r = i / KCH, c = i % KCH;
+        u32x4 t = {0u, 0u, 0u, 0u};
+        if (r < valid) t = *reinterpret_cast<const u32x4*>(kg + (int64_t)r * D + 8 * c);
+        *reinterpret_cast<u32x4*>(k_lds + k_lds_off<D, KT>(r, c)) = t;
+    }
+}
+
+// Stage a V tile transposed. Each lane moves 4 consecutive keys x 8 channels:
+// four 16-byte row loads, a 4x8 -> 8x4 transpose with byte permutes, eight
+// 8-byte LDS writes. The lane -> (key group, chunk) map puts, in every 16-lane
+// write group, 8 distinct swizzles x both halves of a 16-byte chunk.
+template <int D, int KT, int THREADS>
+__device__ __forceinline__ void stage_v_tile(uint8_t* v_lds, const uint16_t* vg, int valid, int tid) {
+    constexpr int WAVES = THREADS / 64;
+    constexpr int GPW = (D == 128) ? 4 : 8;                 // key groups per wave step
+    constexpr int STEPS = (KT / 4) / (GPW * WAVES);
+    static_assert(STEPS * GPW * WAVES == KT / 4, "V tile must split evenly over the waves");
+    const int lane = tid & 63, w = tid >> 6;
+#pragma unroll
+    for (int u = 0; u < STEPS; ++u) {
+        int g4, c;
+        if (D == 128) {
+            g4 = ((lane >> 5) & 1) + 2 * ((lane >> 3) & 1) + GPW * (w + WAVES * u);
+            c = (lane & 7) + 8 * ((lane >> 4) & 1);
+        } else {
+            g4 = ((lane >> 4) & 1) + 2 * ((lane >> 3) & 1) + 4 * ((lane >> 5) & 1) + GPW * (w + WAVES * u);
+            c = lane & 7;
+        }
+        u32x4 rows[4];
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+            int r = 4 * g4 + rr;
+            rows[rr] = u32x4{0u, 0u, 0u, 0u};
+            if (r < valid) rows[rr] = *reinterpret_cast<const u32x4*>(vg + (int64_t)r * D + 8 * c);
+        }
+        const int key = 4 * g4;
+        const int pos = (key & ~12) | ((key & 4) << 1) | ((key & 8) >> 1);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+            u32x2 out;
+            out.x = __builtin_amdgcn_perm(rows[1][e >> 1], rows[0][e >> 1], sel);
+            out.y = __builtin_amdgcn_perm(rows[3][e >> 1], rows[2][e >> 1], sel);
+            const int d = 8 * c + e;
+            *reinterpret_cast<u32x2*>(v_lds + v_lds_off<D, KT>(d, pos >> 3) + (pos & 7) * 2) = out;
+        }
+    }
+}
+
+// Q fragment of one wave: lane holds channels 16 kk + 8 (lane >> 5) + [0, 8) of
+// its query row (zeros when the row is absent).
+template <int D>
+__device__ __forceinline__ void load_q_frag(bf16x8 (&qf)[D / 16], const uint16_t* qrow, bool ok, int half) {
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+        u32x4 t = {0u, 0u, 0u, 0u};
+        if (ok) t = *reinterpret_cast<const u32x4*>(qrow + 16 * kk + 8 * half);
+        qf[kk] = __builtin_bit_cast(bf16x8, t);
+    }
+}
+
+// S^T for one tile: s[st] accumulators as described above.
+template <int D, int KT>
+__device__ __forceinline__ void tile_scores(f32x16 (&s)[KT / 32], const uint8_t* k_lds, const bf16x8 (&qf)[D / 16],
+                                            int l32, int half) {
+#pragma unroll
+    for (int st = 0; st < KT / 32; ++st) {
+        s[st] = f32x16{};
+        const int r = 32 * st + l32;
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk) {
+            u32x4 kv = *reinterpret_cast<const u32x4*>(k_lds + k_lds_off<D, KT>(r, 2 * kk + half));
+            s[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kv), qf[kk], s[st], 0, 0, 0);
+        }
+    }
+}
+
+// O^T += V^T P^T for one tile.
+template <int D, int KT>
+__device__ __forceinline__ void tile_pv(f32x16 (&o)[D / 32], const uint8_t* v_lds, const bf16x8 (&pf)[KT / 32][2],
+                                        int l32, int half) {
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) {
+        const int d = 32 * dt + l32;
+#pragma unroll
+        for (int st = 0; st < KT / 32; ++st)
+#pragma unroll
+            for (int g = 0; g < 2; ++g) {
+                u32x4 vv = *reinterpret_cast<const u32x4*>(v_lds + v_lds_off<D, KT>(d, 4 * st + 2 * g + half));
+                o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vv), pf[st][g], o[dt], 0, 0, 0);
+            }
+    }
+}
+
+__device__ __forceinline__ int acc_key(int st, int x, int half) {
+    return 32 * st + 8 * (x >> 2) + 4 * half + (x & 3);
+}
+
+__device__ __forceinline__ float swap_halves(float x) { return __shfl_xor(x, 32); }
+
+}  // namespace vsa

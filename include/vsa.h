@@ -1,0 +1,231 @@
+/*
+ * vsa.h - block-sparse attention over a 3D (frames x height x width) video token
+ * grid, on AMD Instinct MI355X (gfx950).
+ *
+ * One C-ABI shared library, libvsa.so. Every entry point is extern "C", takes
+ * plain pointers and sizes, and returns an int status (enum vsa_status).
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * Ownership   Every tensor pointer is DEVICE memory owned by the caller, except
+ *             arguments marked "host". The library never allocates or frees
+ *             device memory and keeps no state between calls.
+ * Streams     `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *             Calls are asynchronous on that stream; results are valid once the
+ *             caller synchronises it.
+ * Layout      Q, K, V, O are contiguous [B, H, N, D] row-major (D fastest) with
+ *             16-byte-aligned base pointers. Token n of a T x Hh x W grid sits at
+ *             n = (t*Hh + y)*W + x in natural order.
+ * Blocks      A blocked layout of N positions with block size bs has
+ *             nb = ceil(N / bs) blocks; block b covers positions
+ *             [b*bs, min((b+1)*bs, N)). An optional blk_len[nb] (device int32)
+ *             marks only the first blk_len[b] positions of block b as valid
+ *             (cube padding); NULL means every existing position is valid.
+ * dtype       VSA_BF16 (bfloat16) everywhere; VSA_F32 additionally accepted by
+ *             vsa_block_sparse_attn_fwd and vsa_permute.
+ * Errors      Arguments are validated on the host BEFORE any HIP call; a bad
+ *             argument returns VSA_ERR_INVALID or VSA_ERR_UNSUPPORTED and leaves
+ *             outputs untouched. A failed launch returns VSA_ERR_LAUNCH. The
+ *             message of the last non-zero status of the calling thread is
+ *             returned by vsa_last_error(). Device-side data (index lists, masks,
+ *             blk_len contents) is not validated on the hot path;
+ *             vsa_check_block_list_host validates a list copied to the host.
+ *             No C++ exception crosses this interface.
+ * Determinism Results are bit-reproducible from run to run: no floating-point
+ *             atomics; every reduction has a fixed order.
+ */
+#ifndef VSA_H
+#define VSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum vsa_status {
+    VSA_OK = 0,
+    VSA_ERR_INVALID = 1,      /* invalid argument (null pointer, bad size, ...) */
+    VSA_ERR_UNSUPPORTED = 2,  /* valid but not implemented (dtype, D, bs)       */
+    VSA_ERR_LAUNCH = 3,       /* a HIP launch or runtime call failed            */
+    VSA_ERR_WORKSPACE = 4     /* workspace missing or smaller than required     */
+};
+
+enum vsa_dtype { VSA_BF16 = 0, VSA_F32 = 1 };
+
+/* Token orders (vsa_permute). */
+enum vsa_perm_kind {
+    VSA_PERM_FRAME_MAJOR = 0, /* all frames of one (y, x) contiguous, ordered by t */
+    VSA_PERM_CUBE4 = 1        /* 4x4x4 cubes, each padded to 64 slots             */
+};
+
+/* Token patterns (vsa_pattern_mask). */
+enum vsa_pattern {
+    VSA_PATTERN_SPATIAL = 0,  /* |t_q - t_k| <= w, stated in natural order          */
+    VSA_PATTERN_TEMPORAL = 1  /* |s_q - s_k| <= w, s = y*W + x, in frame-major order */
+};
+
+typedef struct { int32_t T, Hh, W; } vsa_grid;
+
+/* Block sets for vsa_block_sparse_attn_fwd: exactly one of `mask` or
+ * (`kv_idx`, `kv_cnt`) is non-NULL.
+ *   mask    uint8 [B, H, nqb, nkb]: 1 = compute this (query block, key block) tile.
+ *   kv_idx  int32 [B, H, nqb, max_kv]: kept key blocks of each query block; the
+ *           first kv_cnt entries are used, in the order given (ascending keeps
+ *           results identical to the mask form). Entries must lie in [0, nkb).
+ *   kv_cnt  int32 [B, H, nqb]; values above max_kv are clamped to max_kv. */
+typedef struct {
+    const uint8_t* mask;
+    const int32_t* kv_idx;
+    const int32_t* kv_cnt;
+    int32_t max_kv;
+} vsa_blocks;
+
+const char* vsa_status_string(int status);
+const char* vsa_last_error(void);
+/* Library version as 10000*major + 100*minor + patch. */
+int vsa_version(void);
+/* Host-only self-check of the library's integer index helpers (constant-divisor
+ * division used by the layout maps). Returns VSA_OK or VSA_ERR_INVALID. */
+int vsa_selftest_host(void);
+
+/* Number of 4x4x4 cubes of a grid and padded slot count (= 64 * cubes). Host only.
+ * Cubes: USV page, Figure 2 caption (queries, keys and values partitioned into
+ * local 3D cubes). */
+int vsa_cube_dims(vsa_grid g, int32_t* n_cubes, int32_t* n_slots);
+
+/* Any-rule block mask of a token pattern.
+ * Sparse Video-Gen page, "Approach": spatial heads attend block-wise inside a
+ * frame; temporal heads attend to the same position across frames, made
+ * contiguous by the frame-major layout. A (query block, key block) pair is kept
+ * iff some token pair in it satisfies the pattern.
+ *   g, bs    grid and block size (1 <= bs <= 1024); nb = ceil(T*Hh*W / bs)
+ *   pattern  VSA_PATTERN_SPATIAL (natural order) or VSA_PATTERN_TEMPORAL
+ *            (frame-major order); w >= 0 is the window half-width
+ *   mask     out, device uint8 [nb, nb] */
+int vsa_pattern_mask(vsa_grid g, int bs, int pattern, int w, uint8_t* mask, void* stream);
+
+/* Valid token count of each 4x4x4 cube (cube layout of vsa_permute).
+ *   blk_len  out, device int32 [n_cubes] (see vsa_cube_dims) */
+int vsa_cube_block_len(vsa_grid g, int32_t* blk_len, void* stream);
+
+/* Token permutation of Q, K, V or O.
+ * Sparse Video-Gen page, "Approach" (token-major to frame-major layout
+ * transformation) and USV page, Figure 2 caption (3D cube partition).
+ *   VSA_PERM_FRAME_MAJOR  forward: dst[h, s*T + t] = src[h, (t*Hh + y)*W + x]
+ *                         with s = y*W + x; inverse: the reverse move. src and
+ *                         dst are [B, H, N, D]. Heads with head_sel[h] == 0 are
+ *                         copied unchanged; head_sel is a host uint8 [H] (H <= 1024)
+ *                         or NULL for all heads.
+ *   VSA_PERM_CUBE4        forward: src [B, H, N, D] -> dst [B, H, n_slots, D];
+ *                         token (t, y, x) goes to slot 64*c + r, c the raster
+ *                         index of cube (t/4, y/4, x/4), r its rank among the
+ *                         cube's valid tokens in (t, y, x) order; pad slots are
+ *                         zero-filled. inverse: [B, H, n_slots, D] -> [B, H, N, D].
+ *                         head_sel must be NULL.
+ *   dtype VSA_BF16 or VSA_F32; D in {64, 128}. src and dst must not overlap.
+ *   Bit-exact: pure data movement. */
+int vsa_permute(const void* src, void* dst, int B, int H, vsa_grid g, int D, int dtype,
+                int kind, int inverse, const uint8_t* head_sel, void* stream);
+
+/* Block mean-pooling and pooled scores.
+ * USV page, Figure 2 caption: long-range key cubes are chosen by top-k cube
+ * selection; the score is read as scale * <mean of the query block's valid
+ * rows, mean of the key block's valid rows>.
+ *   q, k      [B, H, N, D] bf16 (blocked layout, block size bs in {64, 128})
+ *   blk_len   optional device int32 [nb]
+ *   scale     > 0 (1/sqrt(D) for the attention scale)
+ *   scores    out, device fp32 [B, H, nb, nb]
+ *   qpool, kpool  out, device fp32 [B, H, nb, D] (required; mean vectors; a block
+ *             with no valid row pools to 0). Accumulation in fp32. */
+int vsa_block_scores(const void* q, const void* k, int B, int H, int N, int D, int dtype, int bs,
+                     const int32_t* blk_len, float scale, float* scores, float* qpool,
+                     float* kpool, void* stream);
+
+/* Forced + top-k / top-p block selection, one row per (b, h, query block).
+ * USV page, Figure 2 caption (top-k cube selection beside local attention) and
+ * Sparse VideoGen2 page, Abstract (top-p dynamic budget control).
+ * Per row: forced blocks outrank all others; within each group blocks rank by
+ * score (higher first, equal scores by lower index). If the forced count is
+ * >= k_max the best k_max forced blocks are kept. Otherwise the non-forced
+ * candidates are taken in rank order: with top_p < 1 the shortest prefix
+ * (length >= 1) whose softmax mass (softmax over all nkb scores of the row)
+ * reaches top_p, else all of them, capped at k_max - forced. Output ascending.
+ *   scores   device fp32 [B, H, nqb, nkb]   (1 <= nkb <= 4096)
+ *   forced   device uint8 [nqb, nkb] shared by all (b, h), or NULL
+ *   k_max    1 <= k_max <= nkb;  top_p in (0, 1] (1 = off)
+ *   kv_idx   out, device int32 [B, H, nqb, k_max] (entries past kv_cnt unspecified)
+ *   kv_cnt   out, device int32 [B, H, nqb]
+ * Arithmetic in fp32 (softmax and cumulative mass), ties exact. */
+int vsa_select_topk(const float* scores, int B, int H, int nqb, int nkb, const uint8_t* forced,
+                    int k_max, float top_p, int32_t* kv_idx, int32_t* kv_cnt, void* stream);
+
+/* Per-head pattern choice from sampled query rows.
+ * Sparse Video-Gen page, "Approach" and "Key results": about 1 % of query rows,
+ * each candidate pattern's output compared with dense attention, the
+ * lower-error pattern chosen per head.
+ *   q, k, v     [B, H, N, D] bf16 in NATURAL order, N = T*Hh*W, D = 128
+ *   bs          block size of the candidate masks (64 or 128)
+ *   rows        device int32 [R]: sampled natural query rows (distinct, < N)
+ *   cand_masks  device uint8 [P, nb, nb]; cand_layout host int32 [P]: 0 = the mask
+ *               is stated in natural order, 1 = in frame-major order (evaluated
+ *               through the layout map, no tensor is moved). 1 <= P <= 4.
+ *   err         out, device fp32 [B, H, P]: sum over rows and channels of
+ *               (o_candidate - o_dense)^2, outputs in fp32
+ *   choice      out, device int32 [B, H]: argmin of err, ties to the lowest index
+ *   workspace   device scratch of at least vsa_profile_workspace_bytes(...) bytes */
+size_t vsa_profile_workspace_bytes(int B, int H, vsa_grid g, int D, int R, int P);
+int vsa_profile_heads(const void* q, const void* k, const void* v, int B, int H, vsa_grid g,
+                      int D, int dtype, int bs, const int32_t* rows, int R,
+                      const uint8_t* cand_masks, const int32_t* cand_layout, int P, float scale,
+                      float* err, int32_t* choice, void* workspace, size_t ws_bytes,
+                      void* stream);
+
+/* Mask -> compacted block list (ascending indices of the 1s of each row).
+ *   mask           device uint8: [B, H, nqb, nkb] when head_mask_idx is NULL;
+ *                  otherwise [P, nqb, nkb] and head h of every batch uses
+ *                  mask[head_mask_idx[h]] (host int32 [H], H <= 1024, each < P)
+ *   max_kv         capacity of a row of kv_idx (1 <= max_kv <= nkb); rows with
+ *                  more kept blocks keep their first max_kv
+ *   kv_idx, kv_cnt out, as in vsa_blocks */
+int vsa_mask_to_list(const uint8_t* mask, int B, int H, int nqb, int nkb,
+                     const int32_t* head_mask_idx, int P, int max_kv, int32_t* kv_idx,
+                     int32_t* kv_cnt, void* stream);
+
+/* Block-sparse attention forward.
+ * machinebrief LVSA article (block-sparse attention), Sparse VideoGen2 page,
+ * Abstract (compute only the critical tokens), OSP-Next page, "Method"
+ * (FlashAttention-compatible sparse attention). For each (b, h) and query i:
+ *   O_i = sum_{j in J(i)} softmax_j(scale * <q_i, k_j>) v_j,
+ *   J(i) = the valid keys of the key blocks kept for query block i / bs,
+ * computed tile by tile with an online (running max and sum) softmax over the
+ * kept blocks, skipping every other tile.
+ *   q, k, v, o  [B, H, N, D]; dtype VSA_BF16 (D in {64, 128}, bs in {64, 128}) or
+ *               VSA_F32 (D in {64, 128}, bs = 64); bf16 uses MFMA with fp32
+ *               accumulation, softmax in fp32, P rounded to bf16 for P.V, O
+ *               rounded to nearest even
+ *   lse         optional out, device fp32 [B, H, N]: log-sum-exp (natural log)
+ *               of each query's kept scores
+ *   blk_len     optional device int32 [nb]
+ *   blocks      host pointer to the block set (nqb = nkb = nb)
+ *   scale       > 0, finite
+ *   workspace   may be NULL when vsa_attn_workspace_bytes returns 0
+ * A query with no kept valid key, or in an invalid (padding) slot, gets O = 0
+ * and LSE = -inf. */
+size_t vsa_attn_workspace_bytes(int B, int H, int N, int bs, int max_kv);
+int vsa_block_sparse_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                              int B, int H, int N, int D, int dtype, int bs,
+                              const int32_t* blk_len, const vsa_blocks* blocks, float scale,
+                              void* workspace, size_t ws_bytes, void* stream);
+
+/* Validates a block list held in HOST memory: every kv_cnt in [0, max_kv], the
+ * first kv_cnt entries of each row strictly ascending and inside [0, nkb).
+ * Returns VSA_OK or VSA_ERR_INVALID (message names the first bad row). */
+int vsa_check_block_list_host(const int32_t* kv_idx, const int32_t* kv_cnt, int64_t rows,
+                              int nkb, int max_kv);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* VSA_H */

@@ -1,0 +1,146 @@
+"""C-ABI checks that need no GPU: libvsa.so loads, exports every function that
+include/vsa.h declares, and rejects bad arguments on the host before any HIP
+call (null pointers with valid sizes never reach a launch)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import block_sparse_attention_vsa_amd as V
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "vsa.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(V.LIB_PATH), reason="libvsa.so not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(vsa_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported_and_bound():
+    names = declared_functions()
+    assert len(names) >= 16
+    lib = V.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+        assert n in V._SIGNATURES, f"binding lacks {n}"
+    # the binding exposes a Python function of the same name for each entry point
+    for n in names:
+        assert callable(getattr(V, n)), n
+
+
+def test_status_strings_and_version():
+    assert V.vsa_status_string(0) == "ok"
+    assert V.vsa_status_string(1) == "invalid argument"
+    assert V.vsa_status_string(99) == "unknown status"
+    assert V.vsa_version() >= 100
+
+
+def test_host_selftest_of_index_helpers():
+    assert V.lib().vsa_selftest_host() == V.VSA_OK
+
+
+def test_cube_dims_on_video_grids():
+    assert V.vsa_cube_dims((21, 30, 52)) == (624, 39936)
+    assert V.vsa_cube_dims((4, 8, 8)) == (4, 256)
+    with pytest.raises(V.VsaError):
+        V.vsa_cube_dims((0, 8, 8))
+
+
+def g(T=4, Hh=8, W=8):
+    return V.vsa_grid(T, Hh, W)
+
+
+def test_attention_validation_before_any_hip_call():
+    L = V.lib()
+    fake = ctypes.c_void_p(0x1000)          # aligned, never dereferenced: validation fails first
+    blk = V.vsa_blocks()
+    blk.mask = 0x1000
+    call = lambda **kw: L.vsa_block_sparse_attn_fwd(
+        kw.get("q", fake), fake, fake, fake, None, kw.get("B", 1), 2, 256, kw.get("D", 128), kw.get("dtype", 0),
+        kw.get("bs", 128), None, ctypes.byref(kw.get("blocks", blk)), kw.get("scale", 0.1), None, 0, None)
+    assert call(q=None) == V.VSA_ERR_INVALID
+    assert "null" in V.vsa_last_error()
+    assert call(q=ctypes.c_void_p(0x1004)) == V.VSA_ERR_INVALID
+    assert call(B=0) == V.VSA_ERR_INVALID
+    assert call(D=96) == V.VSA_ERR_UNSUPPORTED
+    assert call(bs=32) == V.VSA_ERR_UNSUPPORTED
+    assert call(dtype=1, bs=128) == V.VSA_ERR_UNSUPPORTED
+    assert call(dtype=7) == V.VSA_ERR_UNSUPPORTED
+    assert call(scale=0.0) == V.VSA_ERR_INVALID
+    assert call(scale=float("inf")) == V.VSA_ERR_INVALID
+    both = V.vsa_blocks(0x1000, 0x1000, 0x1000, 4)
+    assert call(blocks=both) == V.VSA_ERR_INVALID
+    neither = V.vsa_blocks()
+    assert call(blocks=neither) == V.VSA_ERR_INVALID
+    half = V.vsa_blocks(None, 0x1000, None, 4)
+    assert call(blocks=half) == V.VSA_ERR_INVALID
+    assert "exactly one" in V.vsa_last_error() or "list form" in V.vsa_last_error()
+
+
+def test_permute_validation():
+    L = V.lib()
+    p = ctypes.c_void_p(0x1000)
+    assert L.vsa_permute(None, p, 1, 2, g(), 128, 0, 0, 0, None, None) == V.VSA_ERR_INVALID
+    assert L.vsa_permute(p, p, 1, 2, g(), 80, 0, 0, 0, None, None) == V.VSA_ERR_UNSUPPORTED
+    assert L.vsa_permute(p, p, 1, 2, g(), 128, 3, 0, 0, None, None) == V.VSA_ERR_UNSUPPORTED
+    assert L.vsa_permute(p, p, 1, 2, g(), 128, 0, 5, 0, None, None) == V.VSA_ERR_INVALID
+    assert L.vsa_permute(p, p, 1, 2, g(0), 128, 0, 0, 0, None, None) == V.VSA_ERR_INVALID
+    sel = (ctypes.c_uint8 * 2)(1, 0)
+    assert L.vsa_permute(p, p, 1, 2, g(), 128, 0, 1, 0, ctypes.cast(sel, ctypes.c_void_p), None) == V.VSA_ERR_INVALID
+
+
+def test_scores_select_mask_validation():
+    L = V.lib()
+    p = ctypes.c_void_p(0x1000)
+    assert L.vsa_block_scores(p, p, 1, 2, 256, 128, 0, 96, None, 0.1, p, p, p, None) == V.VSA_ERR_UNSUPPORTED
+    assert L.vsa_block_scores(p, p, 1, 2, 256, 128, 1, 64, None, 0.1, p, p, p, None) == V.VSA_ERR_UNSUPPORTED
+    assert L.vsa_block_scores(p, p, 1, 2, 256, 128, 0, 64, None, 0.1, p, None, p, None) == V.VSA_ERR_INVALID
+    assert L.vsa_select_topk(p, 1, 2, 4, 4, None, 0, 1.0, p, p, None) == V.VSA_ERR_INVALID     # k_max < 1
+    assert L.vsa_select_topk(p, 1, 2, 4, 4, None, 5, 1.0, p, p, None) == V.VSA_ERR_INVALID     # k_max > nkb
+    assert L.vsa_select_topk(p, 1, 2, 4, 4, None, 2, 0.0, p, p, None) == V.VSA_ERR_INVALID     # top_p <= 0
+    assert L.vsa_select_topk(p, 1, 2, 4, 4, None, 2, 1.5, p, p, None) == V.VSA_ERR_INVALID     # top_p > 1
+    assert L.vsa_select_topk(p, 1, 2, 4, 5000, None, 2, 1.0, p, p, None) == V.VSA_ERR_UNSUPPORTED
+    assert L.vsa_mask_to_list(p, 1, 2, 4, 4, None, 0, 0, p, p, None) == V.VSA_ERR_INVALID
+    bad = (ctypes.c_int32 * 2)(0, 3)
+    assert L.vsa_mask_to_list(p, 1, 2, 4, 4, ctypes.cast(bad, ctypes.c_void_p), 2, 4, p, p, None) == V.VSA_ERR_INVALID
+    assert L.vsa_pattern_mask(g(), 0, 0, 1, p, None) == V.VSA_ERR_INVALID
+    assert L.vsa_pattern_mask(g(), 64, 2, 1, p, None) == V.VSA_ERR_INVALID
+    assert L.vsa_pattern_mask(g(), 64, 0, -1, p, None) == V.VSA_ERR_INVALID
+
+
+def test_profile_validation_and_workspace_size():
+    L = V.lib()
+    p = ctypes.c_void_p(0x1000)
+    lay = (ctypes.c_int32 * 2)(0, 1)
+    layp = ctypes.cast(lay, ctypes.c_void_p)
+    ws = V.vsa_profile_workspace_bytes(1, 12, (21, 30, 52), 128, 328, 2)
+    assert ws > 0
+    assert V.vsa_profile_workspace_bytes(1, 12, (21, 30, 52), 96, 328, 2) == 0
+    assert L.vsa_profile_heads(p, p, p, 1, 12, V.vsa_grid(21, 30, 52), 128, 0, 128, p, 328, p, layp, 2, 0.1,
+                               p, p, p, 16, None) == V.VSA_ERR_WORKSPACE
+    assert L.vsa_profile_heads(p, p, p, 1, 12, V.vsa_grid(21, 30, 52), 128, 0, 128, p, 328, p, layp, 5, 0.1,
+                               p, p, p, ws, None) == V.VSA_ERR_INVALID
+    bad = (ctypes.c_int32 * 2)(0, 2)
+    assert L.vsa_profile_heads(p, p, p, 1, 12, V.vsa_grid(21, 30, 52), 128, 0, 128, p, 328, p,
+                               ctypes.cast(bad, ctypes.c_void_p), 2, 0.1, p, p, p, ws, None) == V.VSA_ERR_INVALID
+
+
+def test_check_block_list_host():
+    idx = np.array([[0, 2, 5, -1], [1, 1, 0, 0], [3, -1, -1, -1]], np.int32)
+    V.vsa_check_block_list_host(idx[[0, 2]], np.array([3, 1], np.int32), 6)
+    with pytest.raises(V.VsaError, match="ascending"):
+        V.vsa_check_block_list_host(idx, np.array([3, 2, 1], np.int32), 6)
+    with pytest.raises(V.VsaError, match="outside"):
+        V.vsa_check_block_list_host(idx[[0]], np.array([3], np.int32), 5)
+    with pytest.raises(V.VsaError, match="kv_cnt"):
+        V.vsa_check_block_list_host(idx[[0]], np.array([5], np.int32), 6)
+
+
+def test_attn_workspace_is_not_needed():
+    assert V.vsa_attn_workspace_bytes(1, 12, 32760, 128, 256) == 0
