@@ -1,0 +1,417 @@
+"""Benchmark of block-sparse video attention on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-extra]
+
+One step = one pass of the Sparse VideoGen layer over a Wan-2.1-1.3B-shaped 480p
+layer (B=1, H=12, D=128, 21x30x52 latent tokens, bf16): pattern masks, the 1 %-row
+per-head profiler, frame-major permutation of Q, K, V for temporal heads,
+mask -> block lists, block-sparse attention, inverse permutation of O. Inputs sit
+in HBM before the timed region. Prints one JSON line.
+
+`value` is the step's effective throughput: kept attention flops (4 D per valid
+query-key pair of every kept block) divided by the step time. `roofline`
+describes the attention kernel alone, timed with HIP events on its own stream.
+The cube top-p/top-k layer and the long-horizon layer are timed once per run as
+extra sub-step figures. `cpu_baseline` is the fp64 CPU oracle on a sample of
+query blocks of the same workload, on this host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from workloads import WAN480, WAN480_CUBE, LONG126, make_qkv, profile_rows  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2516.6       # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="skip the cube and long-horizon sub-step timings")
+    ap.add_argument("--cpu-sample-blocks", type=int, default=256, help="query blocks per head for the CPU oracle")
+    ap.add_argument("--cpu-leg", action="store_true", help=argparse.SUPPRESS)
+    ap.add_argument("--choice", type=str, default="", help=argparse.SUPPRESS)
+    return ap.parse_args()
+
+
+# ----------------------------------------------------------------- CPU leg ---
+def _cpu_worker_init():
+    try:
+        from threadpoolctl import threadpool_limits
+        threadpool_limits(1)
+    except Exception:
+        pass
+
+
+_CPU = {}
+
+
+def _cpu_unit(args):
+    from oracle.attention import masked_attention
+    h, qb = args
+    q, k, v, blk_by_head, mask_by_head, bs = (_CPU[x] for x in ("q", "k", "v", "blk", "mask", "bs"))
+    blk = blk_by_head[h]
+    rows = np.nonzero(blk == qb)[0]
+    t0 = time.perf_counter()
+    masked_attention(q[:, h:h + 1], k[:, h:h + 1], v[:, h:h + 1], mask_by_head[h], blk, blk, rows=rows)
+    return time.perf_counter() - t0
+
+
+def cpu_leg(args):
+    """Child program (never touches the GPU): regenerates the step's inputs, builds
+    the two candidate masks with the oracle and times the oracle's attention."""
+    from oracle.masks import pattern_mask
+    w = WAN480
+    q, k, v = make_qkv(w)
+    choice = [int(c) for c in args.choice.split(",")]
+    m_s = pattern_mask(w.grid, w.bs, "spatial", w.extra["w_spatial"])
+    m_t = pattern_mask(w.grid, w.bs, "temporal", w.extra["w_temporal"])
+    print(json.dumps(cpu_baseline(q, k, v, choice, m_s, m_t, args.cpu_sample_blocks)), flush=True)
+
+
+def run_cpu_leg(choice, blocks_per_head):
+    import subprocess
+    cmd = [sys.executable, os.path.abspath(__file__), "--cpu-leg", "--choice", ",".join(str(int(c)) for c in choice),
+           "--cpu-sample-blocks", str(blocks_per_head)]
+    res = subprocess.run(cmd, capture_output=True, text=True, timeout=600)
+    if res.returncode != 0:
+        print(f"bench.py: CPU baseline leg failed:\n{res.stderr[-2000:]}", file=sys.stderr)
+        return None
+    return json.loads(res.stdout.strip().splitlines()[-1])
+
+
+def cpu_baseline(q, k, v, choice, m_s, m_t, blocks_per_head):
+    """Times the oracle's masked attention on a sample of query blocks (all heads,
+    evenly spaced blocks), in a fork pool of one single-threaded worker per core."""
+    import multiprocessing as mp
+    from oracle.layout import frame_major_map
+    w = WAN480
+    bs = w.bs
+    N = w.N
+    blk_nat = np.arange(N) // bs
+    blk_fm = frame_major_map(*w.grid) // bs
+    H = q.shape[1]
+    _CPU.update(q=q.astype(np.float64), k=k.astype(np.float64), v=v.astype(np.float64), bs=bs,
+                blk=[blk_fm if choice[h] else blk_nat for h in range(H)],
+                mask=[m_t if choice[h] else m_s for h in range(H)])
+    nb = w.nb
+    picks = np.unique(np.linspace(0, nb - 1, blocks_per_head).round().astype(int))
+    units = [(h, int(qb)) for h in range(H) for qb in picks]
+    # kept flops of the sample: 4 D per valid (query, key) pair
+    nblk = np.full(nb, bs, np.int64)
+    nblk[-1] = N - (nb - 1) * bs
+    flops = 0.0
+    for h, qb in units:
+        m = m_t if choice[h] else m_s
+        flops += 4.0 * w.D * nblk[qb] * float((m[qb].astype(np.int64) * nblk).sum())
+    cores = min(os.cpu_count() or 1, 16)
+    ctx = mp.get_context("fork")
+    t0 = time.perf_counter()
+    with ctx.Pool(cores, initializer=_cpu_worker_init) as pool:
+        pool.map(_cpu_unit, units, chunksize=1)
+    wall = time.perf_counter() - t0
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"value": flops / wall / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": (f"fp64 numpy oracle masked attention on {len(units)} query blocks "
+                       f"({len(picks)} evenly spaced per head x {H} heads) of the Wan 480p layer with the "
+                       f"step's per-head masks; {flops:.3e} kept flops in {wall:.2f} s wall; "
+                       f"one single-threaded worker per core; host CPU {model}")}
+
+
+# ------------------------------------------------------------------ helpers --
+def kept_flops_from_lists(kv_idx, kv_cnt, N, bs, D, blk_len=None):
+    """4 D * sum over kept (query block, key block) of valid_q * valid_k."""
+    idx = kv_idx.cpu().numpy()
+    cnt = kv_cnt.cpu().numpy()
+    nb = -(-N // bs)
+    if blk_len is None:
+        n = np.full(nb, bs, np.int64)
+        n[-1] = N - (nb - 1) * bs
+    else:
+        n = blk_len.cpu().numpy().astype(np.int64)
+    total = 0.0
+    mv = idx.shape[-1]
+    fi = idx.reshape(-1, nb, mv)
+    fc = cnt.reshape(-1, nb)
+    for u in range(fi.shape[0]):
+        ar = np.arange(mv)[None, :] < fc[u][:, None]
+        kn = np.where(ar, n[np.clip(fi[u], 0, nb - 1)], 0).sum(1)
+        total += float((n * kn).sum())
+    return 4.0 * D * total
+
+
+def source_digest(*names):
+    h = hashlib.sha256()
+    for nme in names:
+        with open(os.path.join(ROOT, "block_sparse_attention_vsa_amd", "csrc", nme), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(kernel_key, digest):
+    """HBM bytes per launch measured with rocprofv3 counters for this exact source
+    (profiles/traffic.json), or None when the kernel changed since."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        rec = json.load(open(path)).get(kernel_key)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_digest") != digest:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+class Timer:
+    """HIP events on the stream the library launches on (torch's current stream)."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.acc = {}
+
+    def ev(self):
+        e = self.torch.cuda.Event(enable_timing=True)
+        e.record()
+        return e
+
+    def add(self, key, e0, e1):
+        self.acc.setdefault(key, []).append((e0, e1))
+
+    def mean_ms(self, key):
+        self.torch.cuda.synchronize()
+        pairs = self.acc.get(key, [])
+        return sum(a.elapsed_time(b) for a, b in pairs) / max(1, len(pairs))
+
+
+# --------------------------------------------------------------------- main --
+def main():
+    args = parse()
+    if args.cpu_leg:
+        cpu_leg(args)
+        return
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); the per-head work "
+              f"shards across GPUs with no exchange, which is not exercised here.", file=sys.stderr)
+        sys.exit(2)
+
+    w = WAN480
+    q_np, k_np, v_np = make_qkv(w)
+    rows_np = profile_rows(w, w.extra["profile_frac"])
+
+    import torch
+    import block_sparse_attention_vsa_amd as V
+    from block_sparse_attention_vsa_amd import pipelines as PL
+
+    dev = torch.device("cuda:0")
+    q = torch.from_numpy(q_np).to(torch.bfloat16).to(dev)
+    k = torch.from_numpy(k_np).to(torch.bfloat16).to(dev)
+    v = torch.from_numpy(v_np).to(torch.bfloat16).to(dev)
+    rows = torch.from_numpy(rows_np).to(dev)
+    B, H, N, D = q.shape
+    bs = w.bs
+    grid = w.grid
+    ws = torch.empty((V.vsa_profile_workspace_bytes(B, H, grid, D, rows.numel(), 2),), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    T = Timer(torch)
+    ws_s, ws_t = w.extra["w_spatial"], w.extra["w_temporal"]
+
+    def step(timed):
+        e0 = T.ev()
+        cand = PL.svg_masks(grid, bs, ws_s, ws_t, dev)
+        e1 = T.ev()
+        _, ch = V.vsa_profile_heads(q, k, v, grid, bs, rows, cand, [0, 1], workspace=ws)
+        e2 = T.ev()
+        sel = ch[0].cpu().tolist()
+        e3 = T.ev()
+        qm = V.vsa_permute(q, grid, V.VSA_PERM_FRAME_MAJOR, False, sel)
+        km = V.vsa_permute(k, grid, V.VSA_PERM_FRAME_MAJOR, False, sel)
+        vm = V.vsa_permute(v, grid, V.VSA_PERM_FRAME_MAJOR, False, sel)
+        e4 = T.ev()
+        idx, cnt = V.vsa_mask_to_list(cand, head_mask_idx=sel, B=B)
+        e5 = T.ev()
+        om = V.vsa_block_sparse_attn_fwd(qm, km, vm, bs, kv_idx=idx, kv_cnt=cnt)
+        e6 = T.ev()
+        o = V.vsa_permute(om, grid, V.VSA_PERM_FRAME_MAJOR, True, sel)
+        e7 = T.ev()
+        if timed:
+            for key, a, b in (("a1_pattern_masks", e0, e1), ("a2_profile", e1, e2), ("choice_sync", e2, e3),
+                              ("a3_permute_qkv", e3, e4), ("a6_mask_to_list", e4, e5), ("a7_attention", e5, e6),
+                              ("a8_permute_o", e6, e7)):
+                T.add(key, a, b)
+        return o, sel, idx, cnt
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        o, sel, idx, cnt = step(True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+
+    flops = kept_flops_from_lists(idx, cnt, N, bs, D)
+    attn_ms = T.mean_ms("a7_attention")
+    attn_tflops = flops / (attn_ms * 1e-3) / 1e12
+    comp = {key: round(T.mean_ms(key), 4) for key in T.acc}
+
+    # dense baselines at the same [B, H, N, D]
+    ones = torch.ones((B, H, w.nb, w.nb), dtype=torch.uint8, device=dev)
+    for _ in range(2):
+        V.vsa_block_sparse_attn_fwd(q, k, v, bs, mask=ones)
+    torch.cuda.synchronize()
+    e0 = T.ev()
+    for _ in range(3):
+        V.vsa_block_sparse_attn_fwd(q, k, v, bs, mask=ones)
+    e1 = T.ev()
+    torch.cuda.synchronize()
+    dense_ours = e0.elapsed_time(e1) / 3
+    dense_sdpa = None
+    try:
+        import torch.nn.functional as F
+        for _ in range(2):
+            F.scaled_dot_product_attention(q, k, v)
+        torch.cuda.synchronize()
+        e0 = T.ev()
+        for _ in range(3):
+            F.scaled_dot_product_attention(q, k, v)
+        e1 = T.ev()
+        torch.cuda.synchronize()
+        dense_sdpa = e0.elapsed_time(e1) / 3
+    except Exception as ex:   # report, do not hide
+        print(f"bench.py: torch SDPA baseline failed: {ex}", file=sys.stderr)
+    dense_ms = min(x for x in (dense_ours, dense_sdpa) if x is not None)
+
+    # permutation bandwidth (a3: 3 tensors, read + write of the moved heads)
+    n_moved = sum(sel)
+    perm_bytes = 3 * 2 * B * n_moved * N * D * 2
+    perm_gbs = perm_bytes / (comp["a3_permute_qkv"] * 1e-3) / 1e9 if n_moved else None
+
+    extra = {}
+    if not args.no_extra:
+        extra = extra_layers(torch, V, PL, T)
+
+    digest = source_digest("attn_fwd.hip", "vsa_internal.h")
+    traffic = stored_traffic("attn_fwd_bf16_d128_kernel<128>/wan480_svg", digest)
+    roofline = {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                "kernel": "attn_fwd_bf16_d128_kernel<128>", "per_launch_flops": flops,
+                "avg_launch_ms": round(attn_ms, 4)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = run_cpu_leg(sel, args.cpu_sample_blocks)
+
+    value = flops / (ms_step * 1e-3) / 1e12
+    out = {
+        "metric": "effective TFLOP/s on kept blocks (bf16), % MFMA peak, speedup vs dense attn",
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "wan2.1-1.3B 480p layer, Sparse VideoGen step (profile 1% rows, spatial w=1 / "
+                               "temporal w=0 per head, frame-major permute, block-sparse attention)",
+                   "B": B, "H": H, "N": N, "D": D, "grid": list(grid), "block": bs,
+                   "heads_temporal": int(n_moved), "kept_block_density": round(float(cnt.sum().item()) / (B * H * w.nb * w.nb), 4)},
+        "pct_mfma_peak_step": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "pct_mfma_peak_kernel": round(100 * attn_tflops / PEAK_BF16_TFLOPS, 2),
+        "speedup_vs_dense_kernel": round(dense_ms / attn_ms, 2),
+        "speedup_vs_dense_step": round(dense_ms / ms_step, 2),
+        "dense_ms": {"ours_all_blocks": round(dense_ours, 3), "torch_sdpa": None if dense_sdpa is None else round(dense_sdpa, 3)},
+        "components_ms": comp,
+        "permute_GBps": None if perm_gbs is None else round(perm_gbs, 1),
+        "extra_layers": extra,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def extra_layers(torch, V, PL, T):
+    """Cube top-p/top-k layer (Wan shape) and long-horizon layer, each timed over a
+    few runs with per-call events: the pooling/score and selection steps live here."""
+    res = {}
+    dev = torch.device("cuda:0")
+    w = WAN480_CUBE
+    q, k, v = (torch.from_numpy(x).to(torch.bfloat16).to(dev) for x in make_qkv(w))
+    n_cubes, k_max = PL.cube_budget(w.grid, w.extra["k_frac"])
+    blk = V.vsa_cube_block_len(w.grid)
+    times = {}
+    for rep in range(4):
+        e = [T.ev()]
+        qc = V.vsa_permute(q, w.grid, V.VSA_PERM_CUBE4)
+        kc = V.vsa_permute(k, w.grid, V.VSA_PERM_CUBE4)
+        vc = V.vsa_permute(v, w.grid, V.VSA_PERM_CUBE4)
+        e.append(T.ev())
+        S, _, _ = V.vsa_block_scores(qc, kc, 64, blk_len=blk)
+        e.append(T.ev())
+        idx, cnt = V.vsa_select_topk(S, k_max, w.extra["top_p"])
+        e.append(T.ev())
+        oc = V.vsa_block_sparse_attn_fwd(qc, kc, vc, 64, kv_idx=idx, kv_cnt=cnt, blk_len=blk)
+        e.append(T.ev())
+        o = V.vsa_permute(oc, w.grid, V.VSA_PERM_CUBE4, inverse=True)
+        e.append(T.ev())
+        torch.cuda.synchronize()
+        if rep:
+            for key, i in (("a3_cube_permute_qkv", 0), ("a4_block_scores", 1), ("a5_select_topk", 2),
+                           ("a7_attention", 3), ("a8_cube_permute_o", 4)):
+                times.setdefault(key, []).append(e[i].elapsed_time(e[i + 1]))
+    fl = kept_flops_from_lists(idx, cnt, oc.shape[2], 64, 128, blk)
+    t_att = float(np.mean(times["a7_attention"]))
+    res["cube_topp_wan480"] = {"ms": {k_: round(float(np.mean(v_)), 4) for k_, v_ in times.items()},
+                               "k_max": k_max, "mean_kept": round(float(cnt.float().mean().item()), 2),
+                               "attn_tflops": round(fl / (t_att * 1e-3) / 1e12, 2)}
+    del q, k, v, qc, kc, vc, oc, o, S
+    torch.cuda.empty_cache()
+
+    w = LONG126
+    q, k, v = (torch.from_numpy(x).to(torch.bfloat16).to(dev) for x in make_qkv(w))
+    k_total = int(round(w.extra["density"] * w.nb))
+    times = {}
+    for rep in range(3):
+        e = [T.ev()]
+        forced = V.vsa_pattern_mask(w.grid, w.bs, V.VSA_PATTERN_SPATIAL, w.extra["w_local"])
+        e.append(T.ev())
+        S, _, _ = V.vsa_block_scores(q, k, w.bs)
+        e.append(T.ev())
+        idx, cnt = V.vsa_select_topk(S, k_total, 1.0, forced=forced)
+        e.append(T.ev())
+        o = V.vsa_block_sparse_attn_fwd(q, k, v, w.bs, kv_idx=idx, kv_cnt=cnt)
+        e.append(T.ev())
+        torch.cuda.synchronize()
+        if rep:
+            for key, i in (("a1_local_mask", 0), ("a4_block_scores", 1), ("a5_select_topk", 2), ("a7_attention", 3)):
+                times.setdefault(key, []).append(e[i].elapsed_time(e[i + 1]))
+    fl = kept_flops_from_lists(idx, cnt, w.N, w.bs, 128)
+    t_att = float(np.mean(times["a7_attention"]))
+    res["long_horizon_126x30x52"] = {"ms": {k_: round(float(np.mean(v_)), 4) for k_, v_ in times.items()},
+                                     "k_total": k_total, "attn_tflops": round(fl / (t_att * 1e-3) / 1e12, 2),
+                                     "pct_mfma_peak": round(100 * fl / (t_att * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2)}
+    del q, k, v, o, S
+    torch.cuda.empty_cache()
+    return res
+
+
+if __name__ == "__main__":
+    main()

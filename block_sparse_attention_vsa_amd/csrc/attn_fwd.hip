@@ -203,6 +203,209 @@ __global__ __launch_bounds__(BS * 2) void attn_fwd_bf16_kernel(AttnArgs a) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// bf16, D = 128: the main kernel.
+//
+// Per workgroup one query block (BS rows, BS/32 waves of 32 rows); the kept key
+// blocks are walked in 64-key sub-tiles, double-buffered in LDS:
+//  * K and V sub-tiles go from HBM straight into LDS with global_load_lds_dwordx4
+//    (lane l of a wave instruction lands at base + 16 l), so no VGPRs or VALU
+//    instructions are spent staging tiles, and the next sub-tile streams in while
+//    the current one is computed. Each lane picks the global 16-byte chunk that
+//    belongs at its LDS slot, which realises an XOR swizzle of the chunks:
+//    K row r keeps chunk c at slot c ^ (r & 15), V row r at slot c ^ 4 (r & 3).
+//  * K is read with ds_read_b128 (16 consecutive keys hit 16 distinct slots).
+//  * V stays row-major; the MFMA operand V^T comes from ds_read_b64_tr_b16: in a
+//    16-lane group, lanes 4j..4j+3 point at 16 consecutive channels of key j, and
+//    lane i receives channel i of the four keys. Two such reads give a lane the
+//    8 keys that the P^T operand holds in the same k slots.
+//  * Softmax keeps a running offset m per query that only moves when a tile's
+//    max exceeds it by more than 8 (log2 units), so O is rarely rescaled; p stays
+//    below 2^8 and the final O / l is unchanged.
+template <int BS>
+__global__ __launch_bounds__(BS * 2) __attribute__((amdgpu_waves_per_eu(2))) void attn_fwd_bf16_d128_kernel(AttnArgs a) {
+    constexpr int D = 128, KT = 64;
+    constexpr int WAVES = BS / 32, THREADS = WAVES * 64, SUB = BS / KT;
+    constexpr int TILE = KT * D * 2;                 // bytes of one K or V sub-tile
+    constexpr int INS = TILE / 1024;                 // 1 KiB wave instructions per sub-tile
+    constexpr float TAU = 8.f;
+
+    __shared__ __attribute__((aligned(1024))) uint8_t tiles[2][2][TILE];   // [stage][K, V]
+    __shared__ int16_t list_lds[kMaxMaskBlocks];
+    __shared__ int wave_cnt[WAVES];
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int l32 = lane & 31, half = lane >> 5;
+    const int nqb = a.nb, nkb = a.nb;
+    const int item = xcd_remap(blockIdx.x, a.num_items);
+    const int bh = item / nqb, qb = item - bh * nqb;
+    const int64_t head_off = (int64_t)bh * a.N * D;
+    const int valid_q = block_valid(a.blk_len, qb, BS, a.N);
+    const bool wave_active = 32 * w < valid_q;
+
+    int cnt;
+    const int32_t* list_g = nullptr;
+    if (a.mask) {
+        cnt = compact_mask_row<THREADS>(a.mask + (int64_t)item * nkb, nkb, list_lds, wave_cnt);
+    } else {
+        cnt = min(a.kv_cnt[item], a.max_kv);
+        list_g = a.kv_idx + (int64_t)item * a.max_kv;
+    }
+    auto block_of = [&](int it) -> int {
+        int kb = a.mask ? (int)list_lds[it] : list_g[it];
+        return ((unsigned)kb < (unsigned)nkb) ? kb : -1;    // malformed entries are skipped
+    };
+    // valid keys of sub-tile i (0 when it holds none, or its block entry is malformed)
+    auto sub_valid = [&](int i, int& kb) -> int {
+        kb = block_of(i / SUB);
+        if (kb < 0) return 0;
+        int v = block_valid(a.blk_len, kb, BS, a.N) - (i % SUB) * KT;
+        return v < 0 ? 0 : (v > KT ? KT : v);
+    };
+    auto issue = [&](int i, int stage) {
+        int kb;
+        const int vs = sub_valid(i, kb);
+        if (vs == 0) return;
+        const int64_t row0 = head_off + ((int64_t)kb * BS + (i % SUB) * KT) * D;
+        const uint16_t* kg = a.k + row0;
+        const uint16_t* vg = a.v + row0;
+        const int p = lane & 15;
+#pragma unroll
+        for (int ins = w; ins < INS; ins += WAVES) {
+            const int row = 4 * ins + (lane >> 4);
+            const int rr = row < vs ? row : vs - 1;           // stay inside existing rows
+            __builtin_amdgcn_global_load_lds(kg + (int64_t)rr * D + 8 * (p ^ (row & 15)),
+                (__attribute__((address_space(3))) void*)(&tiles[stage][0][ins * 1024]), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(vg + (int64_t)rr * D + 8 * (p ^ (4 * (row & 3))),
+                (__attribute__((address_space(3))) void*)(&tiles[stage][1][ins * 1024]), 16, 0, 0);
+        }
+    };
+
+    const int q_local = 32 * w + l32;
+    const int q_row = qb * BS + q_local;
+    const bool q_ok = q_local < valid_q;
+    bf16x8 qf[D / 16];
+    load_q_frag<D>(qf, a.q + head_off + (int64_t)q_row * D, q_ok, half);
+
+    f32x16 o_acc[D / 32];
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) o_acc[dt] = f32x16{};
+    float m_run = -INFINITY, l_run = 0.f;
+
+    const int n_sub = cnt * SUB;
+    if (n_sub > 0) issue(0, 0);
+    for (int i = 0; i < n_sub; ++i) {
+        const int stage = i & 1;
+        __builtin_amdgcn_s_waitcnt(0);          // this thread's copies of sub-tile i have landed
+        __syncthreads();                        // ... and everyone's; stage ^ 1 is free again
+        if (i + 1 < n_sub) issue(i + 1, stage ^ 1);
+        int kb;
+        const int vs = sub_valid(i, kb);
+        if (!wave_active || vs == 0) continue;
+        const uint8_t* kt = tiles[stage][0];
+        const uint8_t* vt = tiles[stage][1];
+
+        // ---- S^T = K Q^T (2 x 32 keys) ----------------------------------------
+        f32x16 s[2];
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+            s[st] = f32x16{};
+            const int r = 32 * st + l32;
+#pragma unroll
+            for (int kk = 0; kk < D / 16; ++kk) {
+                u32x4 kv = *reinterpret_cast<const u32x4*>(kt + r * D * 2 + (((2 * kk + half) ^ (r & 15)) << 4));
+                s[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kv), qf[kk], s[st], 0, 0, 0);
+            }
+        }
+        if (vs < KT) {
+#pragma unroll
+            for (int st = 0; st < 2; ++st)
+#pragma unroll
+                for (int x = 0; x < 16; ++x)
+                    if (acc_key(st, x, half) >= vs) s[st][x] = -INFINITY;
+        }
+        // ---- online softmax with a lazily moved offset ---------------------------
+        float mx = -INFINITY;
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
+#pragma unroll
+            for (int x = 0; x < 16; ++x) mx = fmaxf(mx, s[st][x]);
+        mx = pair_max(mx);
+        const float m_tile = mx * a.scale_log2;
+        const bool upd = m_tile > m_run + TAU;
+        const float m_new = upd ? m_tile : m_run;
+        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+        if (__ballot(upd)) {
+            const float alpha = exp2f(m_run - m_use);          // 1 where the offset stays
+            l_run *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+                for (int x = 0; x < 16; ++x) o_acc[dt][x] *= alpha;
+        }
+        m_run = m_new;
+        // p in fp32 feeds the row sum (so the log-sum-exp keeps fp32 accuracy);
+        // its bf16 rounding feeds the P V product
+        bf16x8 pf[2][2];
+        float ps[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
+#pragma unroll
+            for (int x = 0; x < 16; ++x) {
+                const float p = exp2f(fmaf(s[st][x], a.scale_log2, -m_use));
+                ps[x & 3] += p;
+                pf[st][x >> 3][x & 7] = (__bf16)p;
+            }
+        l_run += (ps[0] + ps[1]) + (ps[2] + ps[3]);
+
+        // ---- O^T += V^T P^T, V^T through transposing LDS reads -------------------
+        const int G = lane >> 4, gi = lane & 15;
+        const int j = gi >> 2, c = gi & 3;
+        const int h = G >> 1, dhalf = G & 1;
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt) {
+            const int chunk = 4 * dt + 2 * dhalf + (c >> 1);
+#pragma unroll
+            for (int st = 0; st < 2; ++st)
+#pragma unroll
+                for (int g = 0; g < 2; ++g) {
+                    v4i16 part[2];
+#pragma unroll
+                    for (int r2 = 0; r2 < 2; ++r2) {
+                        const int key = 32 * st + 16 * g + 8 * r2 + 4 * h + j;
+                        const uint8_t* ptr = vt + key * D * 2 + ((chunk ^ (4 * (key & 3))) << 4) + (c & 1) * 8;
+                        part[r2] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                            (__attribute__((address_space(3))) v4i16*)(ptr));
+                    }
+                    bf16x8 vop = __builtin_bit_cast(bf16x8, __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7));
+                    o_acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pf[st][g], o_acc[dt], 0, 0, 0);
+                }
+        }
+    }
+
+    const float l_tot = pair_sum(l_run);
+    if (q_row < a.N) {
+        const bool has = q_ok && l_tot > 0.f;
+        const float inv = has ? 1.f / l_tot : 0.f;
+        uint16_t* orow = a.o + head_off + (int64_t)q_row * D;
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                __bf16 b0 = (__bf16)(o_acc[dt][4 * jj + 0] * inv);
+                __bf16 b1 = (__bf16)(o_acc[dt][4 * jj + 1] * inv);
+                __bf16 b2 = (__bf16)(o_acc[dt][4 * jj + 2] * inv);
+                __bf16 b3 = (__bf16)(o_acc[dt][4 * jj + 3] * inv);
+                u32x2 pk;
+                pk.x = (uint32_t)__builtin_bit_cast(uint16_t, b0) | ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16);
+                pk.y = (uint32_t)__builtin_bit_cast(uint16_t, b2) | ((uint32_t)__builtin_bit_cast(uint16_t, b3) << 16);
+                *reinterpret_cast<u32x2*>(orow + 32 * dt + 8 * jj + 4 * half) = pk;
+            }
+        if (a.lse && half == 0)
+            a.lse[(int64_t)bh * a.N + q_row] = has ? (m_run + log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
+    }
+}
+
 // fp32 kernel (block size 64): one thread per query row, K and V tiles in LDS,
 // exact fp32 arithmetic with an online softmax per tile.
 template <int D>
@@ -346,8 +549,8 @@ extern "C" int vsa_block_sparse_attn_fwd(const void* q, const void* k, const voi
     hipStream_t s = as_stream(stream);
     dim3 grid((unsigned)items);
     if (dtype == VSA_BF16) {
-        if (D == 128 && bs == 128) hipLaunchKernelGGL((attn_fwd_bf16_kernel<128, 128>), grid, dim3(256), 0, s, a);
-        else if (D == 128 && bs == 64) hipLaunchKernelGGL((attn_fwd_bf16_kernel<128, 64>), grid, dim3(128), 0, s, a);
+        if (D == 128 && bs == 128) hipLaunchKernelGGL((attn_fwd_bf16_d128_kernel<128>), grid, dim3(256), 0, s, a);
+        else if (D == 128 && bs == 64) hipLaunchKernelGGL((attn_fwd_bf16_d128_kernel<64>), grid, dim3(128), 0, s, a);
         else if (D == 64 && bs == 128) hipLaunchKernelGGL((attn_fwd_bf16_kernel<64, 128>), grid, dim3(256), 0, s, a);
         else hipLaunchKernelGGL((attn_fwd_bf16_kernel<64, 64>), grid, dim3(128), 0, s, a);
     } else {

@@ -141,4 +141,16 @@ __device__ __forceinline__ int acc_key(int st, int x, int half) {
 
 __device__ __forceinline__ float swap_halves(float x) { return __shfl_xor(x, 32); }
 
+// Max / sum of the values held by lanes l and l ^ 32, via v_permlane32_swap
+// (VALU, no LDS round trip). The swap returns the lower-half value in one result
+// and the upper-half value in the other, so both halves add in the same order.
+__device__ __forceinline__ float pair_max(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 }  // namespace vsa

@@ -1,0 +1,87 @@
+"""The three flows of the pages, as sequences of libvsa calls on one stream.
+
+Each function only orders calls to the library's entry points and allocates
+their outputs; every step runs in a HIP kernel.
+
+* svg_layer: Sparse Video-Gen page, "Approach": pattern masks, per-head choice
+  from sampled rows, frame-major permutation of temporal heads, block-sparse
+  attention, inverse permutation.
+* cube_layer: USV page, Figure 2 caption (3D cubes, top-k cube selection) with
+  the top-p budget of the Sparse VideoGen2 page, Abstract.
+* long_layer: machinebrief LVSA article (block-sparse attention at a long
+  horizon): a local window forced, the rest of a fixed budget by pooled score.
+"""
+from __future__ import annotations
+
+import math
+
+from . import (VSA_PATTERN_SPATIAL, VSA_PATTERN_TEMPORAL, VSA_PERM_CUBE4, VSA_PERM_FRAME_MAJOR,
+               vsa_block_scores, vsa_block_sparse_attn_fwd, vsa_cube_block_len, vsa_cube_dims, vsa_mask_to_list,
+               vsa_pattern_mask, vsa_permute, vsa_profile_heads, vsa_select_topk)
+
+
+def svg_masks(grid, bs, w_spatial, w_temporal, device="cuda"):
+    """Candidate masks [2, nb, nb]: 0 = spatial (natural order), 1 = temporal
+    (frame-major order)."""
+    import torch
+    N = grid[0] * grid[1] * grid[2]
+    nb = -(-N // bs)
+    cand = torch.empty((2, nb, nb), dtype=torch.uint8, device=device)
+    vsa_pattern_mask(grid, bs, VSA_PATTERN_SPATIAL, w_spatial, out=cand[0])
+    vsa_pattern_mask(grid, bs, VSA_PATTERN_TEMPORAL, w_temporal, out=cand[1])
+    return cand
+
+
+def svg_layer(q, k, v, grid, bs, w_spatial, w_temporal, rows, scale=None, choice=None, cand=None, workspace=None,
+              stats=None):
+    """Returns (o, choice_host). `choice` [H] (host) skips the profiler; `rows`
+    (device int32) are the sampled query rows otherwise."""
+    B, H = q.shape[:2]
+    if B != 1:
+        raise ValueError("svg_layer permutes heads by a per-head choice; call it per batch entry")
+    if cand is None:
+        cand = svg_masks(grid, bs, w_spatial, w_temporal, q.device)
+    if choice is None:
+        _, ch = vsa_profile_heads(q, k, v, grid, bs, rows, cand, [0, 1], scale=scale, workspace=workspace)
+        choice = ch[0].cpu().tolist()                       # host decision: which heads move
+    sel = [int(c) for c in choice]
+    qm = vsa_permute(q, grid, VSA_PERM_FRAME_MAJOR, False, sel)
+    km = vsa_permute(k, grid, VSA_PERM_FRAME_MAJOR, False, sel)
+    vm = vsa_permute(v, grid, VSA_PERM_FRAME_MAJOR, False, sel)
+    idx, cnt = vsa_mask_to_list(cand, head_mask_idx=sel, B=B)
+    om = vsa_block_sparse_attn_fwd(qm, km, vm, bs, kv_idx=idx, kv_cnt=cnt, scale=scale)
+    o = vsa_permute(om, grid, VSA_PERM_FRAME_MAJOR, True, sel)
+    if stats is not None:
+        stats.update(kv_idx=idx, kv_cnt=cnt, cand=cand)
+    return o, sel
+
+
+def cube_budget(grid, k_frac):
+    n_cubes, _ = vsa_cube_dims(grid)
+    return n_cubes, max(1, int(math.floor(k_frac * n_cubes)))
+
+
+def cube_layer(q, k, v, grid, k_frac, top_p, scale=None, stats=None):
+    """Returns o in natural order."""
+    n_cubes, k_max = cube_budget(grid, k_frac)
+    qc = vsa_permute(q, grid, VSA_PERM_CUBE4)
+    kc = vsa_permute(k, grid, VSA_PERM_CUBE4)
+    vc = vsa_permute(v, grid, VSA_PERM_CUBE4)
+    blk = vsa_cube_block_len(grid, device=q.device)
+    S, _, _ = vsa_block_scores(qc, kc, 64, blk_len=blk, scale=scale)
+    idx, cnt = vsa_select_topk(S, k_max, top_p)
+    oc = vsa_block_sparse_attn_fwd(qc, kc, vc, 64, kv_idx=idx, kv_cnt=cnt, blk_len=blk, scale=scale)
+    o = vsa_permute(oc, grid, VSA_PERM_CUBE4, inverse=True)
+    if stats is not None:
+        stats.update(kv_idx=idx, kv_cnt=cnt, blk_len=blk, scores=S)
+    return o
+
+
+def long_layer(q, k, v, grid, bs, w_local, k_total, scale=None, stats=None):
+    forced = vsa_pattern_mask(grid, bs, VSA_PATTERN_SPATIAL, w_local, device=q.device)
+    S, _, _ = vsa_block_scores(q, k, bs, scale=scale)
+    idx, cnt = vsa_select_topk(S, k_total, 1.0, forced=forced)
+    o = vsa_block_sparse_attn_fwd(q, k, v, bs, kv_idx=idx, kv_cnt=cnt, scale=scale)
+    if stats is not None:
+        stats.update(kv_idx=idx, kv_cnt=cnt, forced=forced, scores=S)
+    return o
