@@ -44,6 +44,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the cube and long-horizon sub-step timings")
     ap.add_argument("--cpu-sample-blocks", type=int, default=256, help="query blocks per head for the CPU oracle")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="after the run, copy a buffer of this many MiB three times (HBM counter calibration)")
     ap.add_argument("--cpu-leg", action="store_true", help=argparse.SUPPRESS)
     ap.add_argument("--choice", type=str, default="", help=argparse.SUPPRESS)
     return ap.parse_args()
@@ -323,6 +325,13 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         cpu = run_cpu_leg(sel, args.cpu_sample_blocks)
+
+    if args.copy_calibration_mib:
+        src = torch.empty((args.copy_calibration_mib << 20,), dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
 
     value = flops / (ms_step * 1e-3) / 1e12
     out = {

@@ -157,14 +157,14 @@ __global__ __launch_bounds__(BS * 2) void attn_fwd_bf16_kernel(AttnArgs a) {
             mx = fmaxf(mx, swap_halves(mx));
             const float m_new = fmaxf(m_run, mx * a.scale_log2);
             const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-            const float alpha = exp2f(m_run - m_use);
+            const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
             float psum = 0.f;
             bf16x8 pf[NST][2];
 #pragma unroll
             for (int st = 0; st < NST; ++st) {
 #pragma unroll
                 for (int x = 0; x < 16; ++x) {
-                    float p = exp2f(fmaf(s[st][x], a.scale_log2, -m_use));
+                    float p = __builtin_amdgcn_exp2f(fmaf(s[st][x], a.scale_log2, -m_use));
                     psum += p;
                     pf[st][x >> 3][x & 7] = (__bf16)p;
                 }
@@ -226,8 +226,7 @@ template <int BS>
 __global__ __launch_bounds__(BS * 2) __attribute__((amdgpu_waves_per_eu(2))) void attn_fwd_bf16_d128_kernel(AttnArgs a) {
     constexpr int D = 128, KT = 64;
     constexpr int WAVES = BS / 32, THREADS = WAVES * 64, SUB = BS / KT;
-    constexpr int TILE = KT * D * 2;                 // bytes of one K or V sub-tile
-    constexpr int INS = TILE / 1024;                 // 1 KiB wave instructions per sub-tile
+    constexpr int TILE = kSubBytes;                  // bytes of one K or V sub-tile
     constexpr float TAU = 8.f;
 
     __shared__ __attribute__((aligned(1024))) uint8_t tiles[2][2][TILE];   // [stage][K, V]
@@ -267,18 +266,7 @@ __global__ __launch_bounds__(BS * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
         const int vs = sub_valid(i, kb);
         if (vs == 0) return;
         const int64_t row0 = head_off + ((int64_t)kb * BS + (i % SUB) * KT) * D;
-        const uint16_t* kg = a.k + row0;
-        const uint16_t* vg = a.v + row0;
-        const int p = lane & 15;
-#pragma unroll
-        for (int ins = w; ins < INS; ins += WAVES) {
-            const int row = 4 * ins + (lane >> 4);
-            const int rr = row < vs ? row : vs - 1;           // stay inside existing rows
-            __builtin_amdgcn_global_load_lds(kg + (int64_t)rr * D + 8 * (p ^ (row & 15)),
-                (__attribute__((address_space(3))) void*)(&tiles[stage][0][ins * 1024]), 16, 0, 0);
-            __builtin_amdgcn_global_load_lds(vg + (int64_t)rr * D + 8 * (p ^ (4 * (row & 3))),
-                (__attribute__((address_space(3))) void*)(&tiles[stage][1][ins * 1024]), 16, 0, 0);
-        }
+        dma_kv_subtile<WAVES>(tiles[stage][0], tiles[stage][1], a.k + row0, a.v + row0, vs, lane, w);
     };
 
     const int q_local = 32 * w + l32;
@@ -307,16 +295,7 @@ __global__ __launch_bounds__(BS * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
 
         // ---- S^T = K Q^T (2 x 32 keys) ----------------------------------------
         f32x16 s[2];
-#pragma unroll
-        for (int st = 0; st < 2; ++st) {
-            s[st] = f32x16{};
-            const int r = 32 * st + l32;
-#pragma unroll
-            for (int kk = 0; kk < D / 16; ++kk) {
-                u32x4 kv = *reinterpret_cast<const u32x4*>(kt + r * D * 2 + (((2 * kk + half) ^ (r & 15)) << 4));
-                s[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kv), qf[kk], s[st], 0, 0, 0);
-            }
-        }
+        sub_scores(s, kt, qf, l32, half);
         if (vs < KT) {
 #pragma unroll
             for (int st = 0; st < 2; ++st)
@@ -336,7 +315,7 @@ __global__ __launch_bounds__(BS * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
         const float m_new = upd ? m_tile : m_run;
         const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
         if (__ballot(upd)) {
-            const float alpha = exp2f(m_run - m_use);          // 1 where the offset stays
+            const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);          // 1 where the offset stays
             l_run *= alpha;
 #pragma unroll
             for (int dt = 0; dt < D / 32; ++dt)
@@ -352,35 +331,21 @@ __global__ __launch_bounds__(BS * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
         for (int st = 0; st < 2; ++st)
 #pragma unroll
             for (int x = 0; x < 16; ++x) {
-                const float p = exp2f(fmaf(s[st][x], a.scale_log2, -m_use));
+                const float p = __builtin_amdgcn_exp2f(fmaf(s[st][x], a.scale_log2, -m_use));
                 ps[x & 3] += p;
                 pf[st][x >> 3][x & 7] = (__bf16)p;
             }
         l_run += (ps[0] + ps[1]) + (ps[2] + ps[3]);
 
         // ---- O^T += V^T P^T, V^T through transposing LDS reads -------------------
-        const int G = lane >> 4, gi = lane & 15;
-        const int j = gi >> 2, c = gi & 3;
-        const int h = G >> 1, dhalf = G & 1;
 #pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt) {
-            const int chunk = 4 * dt + 2 * dhalf + (c >> 1);
+        for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
             for (int st = 0; st < 2; ++st)
 #pragma unroll
-                for (int g = 0; g < 2; ++g) {
-                    v4i16 part[2];
-#pragma unroll
-                    for (int r2 = 0; r2 < 2; ++r2) {
-                        const int key = 32 * st + 16 * g + 8 * r2 + 4 * h + j;
-                        const uint8_t* ptr = vt + key * D * 2 + ((chunk ^ (4 * (key & 3))) << 4) + (c & 1) * 8;
-                        part[r2] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                            (__attribute__((address_space(3))) v4i16*)(ptr));
-                    }
-                    bf16x8 vop = __builtin_bit_cast(bf16x8, __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7));
-                    o_acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pf[st][g], o_acc[dt], 0, 0, 0);
-                }
-        }
+                for (int g = 0; g < 2; ++g)
+                    o_acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sub_vt_operand(vt, dt, st, g, lane),
+                                                                        pf[st][g], o_acc[dt], 0, 0, 0);
     }
 
     const float l_tot = pair_sum(l_run);
@@ -470,12 +435,12 @@ __global__ __launch_bounds__(64) void attn_fwd_f32_kernel(AttnArgs a) {
         }
         const float m_new = fmaxf(m_run, mx);
         const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-        const float alpha = exp2f(m_run - m_use);
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
         l_run *= alpha;
 #pragma unroll
         for (int d = 0; d < D; ++d) ov[d] *= alpha;
         for (int j = 0; j < BS; ++j) {
-            float p = exp2f(s[j] - m_use);
+            float p = __builtin_amdgcn_exp2f(s[j] - m_use);
             l_run += p;
 #pragma unroll
             for (int d = 0; d < D; ++d) ov[d] = fmaf(p, v_lds[j * D + d], ov[d]);

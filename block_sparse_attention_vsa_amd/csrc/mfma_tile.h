@@ -153,4 +153,71 @@ __device__ __forceinline__ float pair_sum(float x) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+
+// ---------------------------------------------------------------------------
+// 64-key sub-tiles for D = 128 staged by DMA (global_load_lds_dwordx4).
+//
+// A wave instruction of global_load_lds_dwordx4 writes lane l's 16 bytes to LDS
+// base + 16 l, i.e. 1 KiB = 4 rows of 256 bytes. Lane l of instruction ins
+// covers row 4 ins + (l >> 4), LDS slot l & 15 of that row, and fetches the
+// global chunk that belongs there:
+//   K: slot p of row r holds chunk p ^ (r & 15)  (16 keys of one chunk: 16 slots)
+//   V: slot p of row r holds chunk p ^ 4 (r & 3) (the transposing reads below hit
+//      every 16-byte slot of a 256-byte row exactly twice per wave)
+// Rows at or past `valid` re-read row valid - 1 (in bounds; masked later).
+constexpr int kSubKeys = 64;
+constexpr int kSubBytes = kSubKeys * 128 * 2;   // one K or V sub-tile, D = 128
+
+template <int WAVES>
+__device__ __forceinline__ void dma_kv_subtile(uint8_t* k_dst, uint8_t* v_dst, const uint16_t* kg,
+                                               const uint16_t* vg, int valid, int lane, int w) {
+    constexpr int D = 128;
+    const int p = lane & 15;
+#pragma unroll
+    for (int ins = w; ins < kSubBytes / 1024; ins += WAVES) {
+        const int row = 4 * ins + (lane >> 4);
+        const int rr = row < valid ? row : valid - 1;
+        __builtin_amdgcn_global_load_lds(kg + (int64_t)rr * D + 8 * (p ^ (row & 15)),
+            (__attribute__((address_space(3))) void*)(k_dst + ins * 1024), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(vg + (int64_t)rr * D + 8 * (p ^ (4 * (row & 3))),
+            (__attribute__((address_space(3))) void*)(v_dst + ins * 1024), 16, 0, 0);
+    }
+}
+
+// S^T for a 64-key sub-tile: s[st] holds keys 32 st + acc_key(0, x, half).
+__device__ __forceinline__ void sub_scores(f32x16 (&s)[2], const uint8_t* kt, const bf16x8 (&qf)[8], int l32,
+                                           int half) {
+    constexpr int D = 128;
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+        s[st] = f32x16{};
+        const int r = 32 * st + l32;
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk) {
+            u32x4 kv = *reinterpret_cast<const u32x4*>(kt + r * D * 2 + (((2 * kk + half) ^ (r & 15)) << 4));
+            s[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kv), qf[kk], s[st], 0, 0, 0);
+        }
+    }
+}
+
+// V^T operand for channel tile dt and keys [32 st + 16 g, +16) of a sub-tile:
+// two ds_read_b64_tr_b16. In a 16-lane group G of the wave, lanes 4j..4j+3
+// point at 16 consecutive channels (32 dt + 16 (G & 1) + [0, 16)) of key
+// 32 st + 16 g + 8 r + 4 (G >> 1) + j; lane i then holds channel i of those four
+// keys, which are the keys of k slots (G >> 1, 4 r + j) of the P^T operand.
+__device__ __forceinline__ bf16x8 sub_vt_operand(const uint8_t* vt, int dt, int st, int g, int lane) {
+    constexpr int D = 128;
+    const int G = lane >> 4, gi = lane & 15;
+    const int j = gi >> 2, c = gi & 3;
+    const int chunk = 4 * dt + 2 * (G & 1) + (c >> 1);
+    v4i16 part[2];
+#pragma unroll
+    for (int r2 = 0; r2 < 2; ++r2) {
+        const int key = 32 * st + 16 * g + 8 * r2 + 4 * (G >> 1) + j;
+        const uint8_t* ptr = vt + key * D * 2 + ((chunk ^ (4 * (key & 3))) << 4) + (c & 1) * 8;
+        part[r2] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(ptr));
+    }
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
 }  // namespace vsa

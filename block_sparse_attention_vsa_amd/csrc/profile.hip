@@ -9,16 +9,19 @@
 //  1. bits: for each candidate p and sampled row r, one bit per natural key n,
 //     set iff M_p[L_p(r) / bs][L_p(n) / bs] != 0, where L_p is the identity
 //     (mask stated in natural order) or the frame-major map (n -> s*T + t).
-//  2. main, once per output slot (dense, then each candidate): workgroups of 4
-//     waves x 32 sampled rows walk a contiguous range of 128-key tiles (split-K
-//     over keys, so that a few hundred rows still fill the chip). Per tile the
-//     scores S^T come from MFMA, the slot's bits mask them, an online softmax
-//     (max, sum) runs and O^T accumulates. Each (slot, row, split) writes a
-//     partial record (m, l, O) to the workspace.
-//  3. merge: partial records are combined in split order (exact log-sum-exp
-//     rescaling), outputs normalised, squared differences to the dense output
-//     summed per 32-row chunk in a fixed order.
-//  4. finish: chunk sums added in order; choice = first argmin.
+//  2. main, in passes of two output slots (dense and candidate 0, then the
+//     next candidates): workgroups of 4 waves x 32 sampled rows walk a
+//     contiguous range of 64-key sub-tiles (split-K over keys, so that a few
+//     hundred rows still fill the chip), with K and V streamed into
+//     double-buffered LDS by DMA. Per sub-tile the scores S^T come from MFMA once
+//     per pass; each slot masks them with its bits, keeps its own online softmax
+//     (max, sum) and accumulates its own O^T. Each (slot, row, split) writes a
+//     partial record (m, l, O).
+//  3. merge: one workgroup per (b, h, sampled row) combines the partial records
+//     in split order (exact log-sum-exp rescaling), normalises every slot and
+//     sums each candidate's squared difference to the dense output.
+//  4. finish: per (b, h) the row sums are added in a fixed tree order; choice =
+//     first argmin.
 #include <math.h>
 
 #include <algorithm>
@@ -27,13 +30,13 @@
 
 namespace vsa {
 
-constexpr int kProfKT = 128;          // keys per tile
-constexpr int kProfRows = 128;        // sampled rows per workgroup
+constexpr int kProfRows = 128;        // sampled rows per workgroup (4 waves x 32)
 constexpr int kProfMaxP = 4;
-constexpr int kProfTargetWG = 1024;
+constexpr int kProfTargetWG = 512;
+constexpr int kProfMaxSlots = 2;      // accumulator sets per pass (more would spill registers)
 
 struct ProfPlan {
-    int ntiles, RT, S, TPS, chunks, words;
+    int nsub, RT, S, TPS, words;
     int64_t rec;                       // floats per partial record
     size_t off_bits, off_part, off_errp, total;
 };
@@ -42,19 +45,18 @@ static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 static ProfPlan prof_plan(int B, int H, int64_t N, int D, int R, int P) {
     ProfPlan p;
-    p.ntiles = (int)((N + kProfKT - 1) / kProfKT);
+    p.nsub = (int)((N + kSubKeys - 1) / kSubKeys);
     p.RT = (R + kProfRows - 1) / kProfRows;
     int64_t per = (int64_t)p.RT * B * H;
-    int S = (int)std::min<int64_t>(16, std::max<int64_t>(1, (kProfTargetWG + per - 1) / per));
-    S = std::min(S, p.ntiles);
-    p.TPS = (p.ntiles + S - 1) / S;
-    p.S = (p.ntiles + p.TPS - 1) / p.TPS;
-    p.chunks = (R + 31) / 32;
-    p.words = p.ntiles * 4;            // 32-key words, padded to whole tiles
+    int S = (int)std::min<int64_t>(32, std::max<int64_t>(1, (kProfTargetWG + per - 1) / per));
+    S = std::min(S, p.nsub);
+    p.TPS = (p.nsub + S - 1) / S;
+    p.S = (p.nsub + p.TPS - 1) / p.TPS;
+    p.words = 2 * p.nsub;              // 32-key words, whole sub-tiles
     p.rec = D + 4;                     // m, l, 2 pad, O[D]
     size_t bits = (size_t)P * R * p.words * 4;
     size_t part = (size_t)(P + 1) * B * H * R * p.S * p.rec * 4;
-    size_t errp = (size_t)B * H * p.chunks * kProfMaxP * 4;
+    size_t errp = (size_t)B * H * R * kProfMaxP * 4;
     p.off_bits = 0;
     p.off_part = align256(bits);
     p.off_errp = p.off_part + align256(part);
@@ -106,19 +108,18 @@ struct ProfArgs {
     const int32_t* rows;
     const uint32_t* bits;
     float* part;
-    int32_t R, N, S, TPS, ntiles, words, BH;
+    int32_t R, N, S, TPS, nsub, words, BH;
     int64_t rec;
     float scale_log2;
-    int32_t slot_out[1];               // output slot (0 = dense, 1 + p = candidate p)
-    int32_t slot_cand[1];              // candidate whose bits apply, -1 = none
+    int32_t slot_out[kProfMaxSlots];   // output slot (0 = dense, 1 + p = candidate p)
+    int32_t slot_cand[kProfMaxSlots];  // candidate whose bits apply, -1 = none
 };
 
-template <int D, int NC>
+template <int NC>
 __global__ __launch_bounds__(256) void prof_main_kernel(ProfArgs a) {
-    constexpr int KT = kProfKT;
-    constexpr int NST = KT / 32, NDT = D / 32;
-    __shared__ __attribute__((aligned(16))) uint8_t k_lds[KT * D * 2];
-    __shared__ __attribute__((aligned(16))) uint8_t v_lds[D * KT * 2];
+    constexpr int D = 128, KT = kSubKeys;
+    constexpr float TAU = 8.f;
+    __shared__ __attribute__((aligned(1024))) uint8_t tiles[2][2][kSubBytes];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int l32 = lane & 31, half = lane >> 5;
     const int split = blockIdx.x, rt = blockIdx.y, bh = blockIdx.z;
@@ -131,78 +132,94 @@ __global__ __launch_bounds__(256) void prof_main_kernel(ProfArgs a) {
     bf16x8 qf[D / 16];
     load_q_frag<D>(qf, a.q + head_off + (int64_t)(row_ok ? r : 0) * D, row_ok, half);
 
-    f32x16 o[NC][NDT];
+    f32x16 o[NC][D / 32];
     float m_run[NC], l_run[NC];
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
         m_run[c] = -INFINITY;
         l_run[c] = 0.f;
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) o[c][dt] = f32x16{};
+        for (int dt = 0; dt < D / 32; ++dt) o[c][dt] = f32x16{};
     }
-    const int t0 = split * a.TPS, t1 = min(t0 + a.TPS, a.ntiles);
+    const int t0 = split * a.TPS, t1 = min(t0 + a.TPS, a.nsub);
+    auto issue = [&](int t, int stage) {
+        const int vs = min(KT, a.N - t * KT);
+        const int64_t row0 = head_off + (int64_t)t * KT * D;
+        dma_kv_subtile<4>(tiles[stage][0], tiles[stage][1], a.k + row0, a.v + row0, vs, lane, w);
+    };
+    if (t0 < t1) issue(t0, 0);
     for (int t = t0; t < t1; ++t) {
-        const int valid = min(KT, a.N - t * KT);
+        const int stage = (t - t0) & 1;
+        __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
-        stage_k_tile<D, KT, 256>(k_lds, a.k + head_off + (int64_t)t * KT * D, valid, tid);
-        stage_v_tile<D, KT, 256>(v_lds, a.v + head_off + (int64_t)t * KT * D, valid, tid);
-        __syncthreads();
+        if (t + 1 < t1) issue(t + 1, stage ^ 1);
         if (!wave_active) continue;
-        f32x16 s[NST];
-        tile_scores<D, KT>(s, k_lds, qf, l32, half);
-        if (valid < KT) {
+        const int vs = min(KT, a.N - t * KT);
+        f32x16 s[2];
+        sub_scores(s, tiles[stage][0], qf, l32, half);
+        if (vs < KT) {
 #pragma unroll
-            for (int st = 0; st < NST; ++st)
+            for (int st = 0; st < 2; ++st)
 #pragma unroll
                 for (int x = 0; x < 16; ++x)
-                    if (acc_key(st, x, half) >= valid) s[st][x] = -INFINITY;
+                    if (acc_key(st, x, half) >= vs) s[st][x] = -INFINITY;
         }
+        const uint8_t* vt = tiles[stage][1];
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
-            uint32_t wbits[NST];
             const int cand = a.slot_cand[c];
+            uint32_t wbits[2] = {0xffffffffu, 0xffffffffu};
+            if (cand >= 0) {
 #pragma unroll
-            for (int st = 0; st < NST; ++st) {
-                wbits[st] = 0xffffffffu;
-                if (cand >= 0)
-                    wbits[st] = row_ok ? a.bits[((int64_t)cand * a.R + ri) * a.words + 4 * t + st] : 0u;
+                for (int st = 0; st < 2; ++st)
+                    wbits[st] = row_ok ? a.bits[((int64_t)cand * a.R + ri) * a.words + 2 * t + st] : 0u;
             }
             float mx = -INFINITY;
 #pragma unroll
-            for (int st = 0; st < NST; ++st)
+            for (int st = 0; st < 2; ++st)
 #pragma unroll
-                for (int x = 0; x < 16; ++x) {
-                    const int bit = 8 * (x >> 2) + 4 * half + (x & 3);
-                    if ((wbits[st] >> bit) & 1u) mx = fmaxf(mx, s[st][x]);
-                }
-            mx = fmaxf(mx, swap_halves(mx));
-            const float m_new = fmaxf(m_run[c], mx * a.scale_log2);
+                for (int x = 0; x < 16; ++x)
+                    if ((wbits[st] >> (8 * (x >> 2) + 4 * half + (x & 3))) & 1u) mx = fmaxf(mx, s[st][x]);
+            mx = pair_max(mx);
+            const float m_tile = mx * a.scale_log2;
+            const bool upd = m_tile > m_run[c] + TAU;
+            const float m_new = upd ? m_tile : m_run[c];
             const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-            const float alpha = exp2f(m_run[c] - m_use);
-            float psum = 0.f;
-            bf16x8 pf[NST][2];
+            if (__ballot(upd)) {
+                const float alpha = __builtin_amdgcn_exp2f(m_run[c] - m_use);
+                l_run[c] *= alpha;
 #pragma unroll
-            for (int st = 0; st < NST; ++st)
+                for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+                    for (int x = 0; x < 16; ++x) o[c][dt][x] *= alpha;
+            }
+            m_run[c] = m_new;
+            bf16x8 pf[2][2];
+            float ps = 0.f;
+#pragma unroll
+            for (int st = 0; st < 2; ++st)
 #pragma unroll
                 for (int x = 0; x < 16; ++x) {
-                    const int bit = 8 * (x >> 2) + 4 * half + (x & 3);
-                    float p = ((wbits[st] >> bit) & 1u) ? exp2f(fmaf(s[st][x], a.scale_log2, -m_use)) : 0.f;
-                    psum += p;
+                    const bool keep = (wbits[st] >> (8 * (x >> 2) + 4 * half + (x & 3))) & 1u;
+                    const float p = keep ? __builtin_amdgcn_exp2f(fmaf(s[st][x], a.scale_log2, -m_use)) : 0.f;
+                    ps += p;
                     pf[st][x >> 3][x & 7] = (__bf16)p;
                 }
-            l_run[c] = l_run[c] * alpha + psum;
-            m_run[c] = m_new;
+            l_run[c] += ps;
 #pragma unroll
-            for (int dt = 0; dt < NDT; ++dt)
+            for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-                for (int x = 0; x < 16; ++x) o[c][dt][x] *= alpha;
-            tile_pv<D, KT>(o[c], v_lds, pf, l32, half);
+                for (int st = 0; st < 2; ++st)
+#pragma unroll
+                    for (int g = 0; g < 2; ++g)
+                        o[c][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sub_vt_operand(vt, dt, st, g, lane),
+                                                                           pf[st][g], o[c][dt], 0, 0, 0);
         }
     }
     if (!wave_active) return;
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-        const float l_tot = l_run[c] + swap_halves(l_run[c]);
+        const float l_tot = pair_sum(l_run[c]);
         if (ri >= a.R) continue;
         float* rec = a.part + ((((int64_t)a.slot_out[c] * a.BH + bh) * a.R + ri) * a.S + split) * a.rec;
         if (half == 0) {
@@ -210,7 +227,7 @@ __global__ __launch_bounds__(256) void prof_main_kernel(ProfArgs a) {
             rec[1] = l_tot;
         }
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt)
+        for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 f32x4 v4 = {o[c][dt][4 * j], o[c][dt][4 * j + 1], o[c][dt][4 * j + 2], o[c][dt][4 * j + 3]};
@@ -222,63 +239,71 @@ __global__ __launch_bounds__(256) void prof_main_kernel(ProfArgs a) {
 struct MergeArgs {
     const float* part;
     float* errp;
-    int32_t R, S, BH, D, P, chunks;
+    int32_t R, S, BH, P;
     int64_t rec;
 };
 
-// One workgroup per (bh, chunk of 32 rows). Thread t handles channel t % D of
-// rows 256 / D apart; partial records are merged in split order.
-__global__ __launch_bounds__(256) void prof_merge_kernel(MergeArgs a) {
-    __shared__ float red[kProfMaxP][256];
-    const int bh = blockIdx.y, chunk = blockIdx.x;
-    const int d = threadIdx.x % a.D;
-    const int rstep = 256 / a.D;
-    float acc[kProfMaxP] = {0.f, 0.f, 0.f, 0.f};
-    for (int rr = threadIdx.x / a.D; rr < 32; rr += rstep) {
-        const int ri = chunk * 32 + rr;
-        if (ri >= a.R) break;
-        float dense = 0.f;
-        for (int slot = 0; slot <= a.P; ++slot) {
-            const float* recs = a.part + (((int64_t)slot * a.BH + bh) * a.R + ri) * a.S * a.rec;
-            float m = -INFINITY;
-            for (int s = 0; s < a.S; ++s) m = fmaxf(m, recs[s * a.rec]);
-            float l = 0.f, ov = 0.f;
-            if (m != -INFINITY) {
-                for (int s = 0; s < a.S; ++s) {
-                    const float ms = recs[s * a.rec];
-                    if (ms == -INFINITY) continue;
-                    const float f = exp2f(ms - m);
-                    l += recs[s * a.rec + 1] * f;
-                    ov += recs[s * a.rec + 4 + d] * f;
-                }
+// One workgroup of D = 128 threads per (b, h, sampled row); thread d merges
+// channel d of every slot over the splits in order.
+__global__ __launch_bounds__(128) void prof_merge_kernel(MergeArgs a) {
+    __shared__ float red[kProfMaxP][128];
+    const int ri = blockIdx.x, bh = blockIdx.y, d = threadIdx.x;
+    float dense = 0.f;
+    for (int slot = 0; slot <= a.P; ++slot) {
+        const float* recs = a.part + (((int64_t)slot * a.BH + bh) * a.R + ri) * a.S * a.rec;
+        float m = -INFINITY;
+        for (int s = 0; s < a.S; ++s) m = fmaxf(m, recs[s * a.rec]);
+        float l = 0.f, ov = 0.f;
+        if (m != -INFINITY) {
+            for (int s = 0; s < a.S; ++s) {
+                const float ms = recs[s * a.rec];
+                if (ms == -INFINITY) continue;
+                const float f = __builtin_amdgcn_exp2f(ms - m);
+                l += recs[s * a.rec + 1] * f;
+                ov += recs[s * a.rec + 4 + d] * f;
             }
-            const float out = l > 0.f ? ov / l : 0.f;
-            if (slot == 0) dense = out;
-            else acc[slot - 1] += (out - dense) * (out - dense);
         }
+        const float out = l > 0.f ? ov / l : 0.f;
+        if (slot == 0) dense = out;
+        else red[slot - 1][d] = (out - dense) * (out - dense);
     }
-    for (int p = 0; p < a.P; ++p) red[p][threadIdx.x] = acc[p];
     __syncthreads();
-    for (int s = 128; s > 0; s >>= 1) {
-        if ((int)threadIdx.x < s)
-            for (int p = 0; p < a.P; ++p) red[p][threadIdx.x] += red[p][threadIdx.x + s];
+    for (int s = 64; s > 0; s >>= 1) {
+        if (d < s)
+            for (int p = 0; p < a.P; ++p) red[p][d] += red[p][d + s];
         __syncthreads();
     }
-    if ((int)threadIdx.x < a.P) a.errp[((int64_t)bh * a.chunks + chunk) * kProfMaxP + threadIdx.x] = red[threadIdx.x][0];
+    if (d < a.P) a.errp[((int64_t)bh * a.R + ri) * kProfMaxP + d] = red[d][0];
 }
 
-__global__ void prof_finish_kernel(const float* errp, int BH, int chunks, int P, float* err, int32_t* choice) {
-    int bh = blockIdx.x * blockDim.x + threadIdx.x;
-    if (bh >= BH) return;
-    int best = 0;
-    float best_e = INFINITY;
+// One workgroup per (b, h): per-row errors summed in a fixed order.
+__global__ __launch_bounds__(256) void prof_finish_kernel(const float* errp, int R, int P, float* err,
+                                                          int32_t* choice) {
+    __shared__ float red[kProfMaxP][256];
+    __shared__ float tot[kProfMaxP];
+    const int bh = blockIdx.x, t = threadIdx.x;
     for (int p = 0; p < P; ++p) {
-        float e = 0.f;
-        for (int c = 0; c < chunks; ++c) e += errp[((int64_t)bh * chunks + c) * kProfMaxP + p];
-        err[(int64_t)bh * P + p] = e;
-        if (e < best_e) { best_e = e; best = p; }
+        float acc = 0.f;
+        for (int ri = t; ri < R; ri += 256) acc += errp[((int64_t)bh * R + ri) * kProfMaxP + p];
+        red[p][t] = acc;
     }
-    choice[bh] = best;
+    __syncthreads();
+    for (int s = 128; s > 0; s >>= 1) {
+        if (t < s)
+            for (int p = 0; p < P; ++p) red[p][t] += red[p][t + s];
+        __syncthreads();
+    }
+    if (t == 0) {
+        int best = 0;
+        float best_e = INFINITY;
+        for (int p = 0; p < P; ++p) {
+            const float e = red[p][0];
+            tot[p] = e;
+            err[(int64_t)bh * P + p] = e;
+            if (e < best_e) { best_e = e; best = p; }
+        }
+        choice[bh] = best;
+    }
 }
 
 }  // namespace vsa
@@ -286,8 +311,7 @@ __global__ void prof_finish_kernel(const float* errp, int BH, int chunks, int P,
 using namespace vsa;
 
 extern "C" size_t vsa_profile_workspace_bytes(int B, int H, vsa_grid g, int D, int R, int P) {
-    if (B <= 0 || H <= 0 || g.T <= 0 || g.Hh <= 0 || g.W <= 0 || R <= 0 || P <= 0 || P > kProfMaxP ||
-        (D != 64 && D != 128))
+    if (B <= 0 || H <= 0 || g.T <= 0 || g.Hh <= 0 || g.W <= 0 || R <= 0 || P <= 0 || P > kProfMaxP || D != 128)
         return 0;
     return prof_plan(B, H, (int64_t)g.T * g.Hh * g.W, D, R, P).total;
 }
@@ -301,8 +325,8 @@ extern "C" int vsa_profile_heads(const void* q, const void* k, const void* v, in
     if (!aligned16(q) || !aligned16(k) || !aligned16(v)) return fail(VSA_ERR_INVALID, "vsa_profile_heads: q, k, v must be 16-byte aligned");
     if (B <= 0 || H <= 0 || g.T <= 0 || g.Hh <= 0 || g.W <= 0) return fail(VSA_ERR_INVALID, "vsa_profile_heads: bad sizes");
     if (dtype != VSA_BF16) return fail(VSA_ERR_UNSUPPORTED, "vsa_profile_heads: only bf16 inputs");
-    if (D != 128 && D != 64) return fail(VSA_ERR_UNSUPPORTED, "vsa_profile_heads: D must be 64 or 128");
-    if (bs != 64 && bs != 128) return fail(VSA_ERR_UNSUPPORTED, "vsa_profile_heads: bs must be 64 or 128");
+    if (D != 128) return fail(VSA_ERR_UNSUPPORTED, "vsa_profile_heads: D must be 128");
+    if (bs < 1 || bs > 1024) return fail(VSA_ERR_INVALID, "vsa_profile_heads: bs must be in [1, 1024]");
     if (P < 1 || P > kProfMaxP) return fail(VSA_ERR_INVALID, "vsa_profile_heads: P must be in [1, %d]", kProfMaxP);
     if (R < 1) return fail(VSA_ERR_INVALID, "vsa_profile_heads: R must be >= 1");
     if (!(scale > 0.f) || !__builtin_isfinite(scale)) return fail(VSA_ERR_INVALID, "vsa_profile_heads: scale must be positive and finite");
@@ -311,7 +335,7 @@ extern "C" int vsa_profile_heads(const void* q, const void* k, const void* v, in
             return fail(VSA_ERR_INVALID, "vsa_profile_heads: cand_layout[%d] must be 0 or 1", p);
     const int64_t N = (int64_t)g.T * g.Hh * g.W;
     if (N >= (1ll << 31) || R > N) return fail(VSA_ERR_INVALID, "vsa_profile_heads: bad N or R");
-    if ((int64_t)B * H > 65535) return fail(VSA_ERR_INVALID, "vsa_profile_heads: B*H too large");
+    if ((int64_t)B * H > 65535 || R > 65535) return fail(VSA_ERR_INVALID, "vsa_profile_heads: B*H or R too large");
     const ProfPlan pl = prof_plan(B, H, N, D, R, P);
     if (!workspace || ws_bytes < pl.total)
         return fail(VSA_ERR_WORKSPACE, "vsa_profile_heads: workspace of %zu bytes needed (got %zu)", pl.total, ws_bytes);
@@ -333,28 +357,30 @@ extern "C" int vsa_profile_heads(const void* q, const void* k, const void* v, in
     ProfArgs pa;
     pa.q = static_cast<const uint16_t*>(q); pa.k = static_cast<const uint16_t*>(k); pa.v = static_cast<const uint16_t*>(v);
     pa.rows = rows; pa.bits = ba.bits; pa.part = reinterpret_cast<float*>(ws + pl.off_part);
-    pa.R = R; pa.N = (int32_t)N; pa.S = pl.S; pa.TPS = pl.TPS; pa.ntiles = pl.ntiles; pa.words = pl.words;
+    pa.R = R; pa.N = (int32_t)N; pa.S = pl.S; pa.TPS = pl.TPS; pa.nsub = pl.nsub; pa.words = pl.words;
     pa.BH = B * H; pa.rec = pl.rec;
     pa.scale_log2 = (float)((double)scale * 1.4426950408889634);
     dim3 grid(pl.S, pl.RT, B * H);
-    // One output slot per pass (dense first, then each candidate): a single set
-    // of accumulators keeps the kernel free of register spills.
-    for (int slot = 0; slot <= P; ++slot) {
-        pa.slot_out[0] = slot;
-        pa.slot_cand[0] = slot - 1;
-        if (D == 128) hipLaunchKernelGGL((prof_main_kernel<128, 1>), grid, dim3(256), 0, s, pa);
-        else hipLaunchKernelGGL((prof_main_kernel<64, 1>), grid, dim3(256), 0, s, pa);
+    // output slots 0 (dense) .. P in passes of up to two accumulator sets
+    for (int first = 0; first <= P; first += kProfMaxSlots) {
+        const int nc = std::min(kProfMaxSlots, P + 1 - first);
+        for (int c = 0; c < kProfMaxSlots; ++c) {
+            const int slot = first + std::min(c, nc - 1);
+            pa.slot_out[c] = slot;
+            pa.slot_cand[c] = slot - 1;
+        }
+        if (nc == 2) hipLaunchKernelGGL(prof_main_kernel<2>, grid, dim3(256), 0, s, pa);
+        else hipLaunchKernelGGL(prof_main_kernel<1>, grid, dim3(256), 0, s, pa);
         st = launch_status("vsa_profile_heads (main)");
         if (st) return st;
     }
 
     MergeArgs ma;
     ma.part = pa.part; ma.errp = reinterpret_cast<float*>(ws + pl.off_errp);
-    ma.R = R; ma.S = pl.S; ma.BH = B * H; ma.D = D; ma.P = P; ma.chunks = pl.chunks; ma.rec = pl.rec;
-    hipLaunchKernelGGL(prof_merge_kernel, dim3(pl.chunks, B * H), dim3(256), 0, s, ma);
+    ma.R = R; ma.S = pl.S; ma.BH = B * H; ma.P = P; ma.rec = pl.rec;
+    hipLaunchKernelGGL(prof_merge_kernel, dim3(R, B * H), dim3(128), 0, s, ma);
     st = launch_status("vsa_profile_heads (merge)");
     if (st) return st;
-    hipLaunchKernelGGL(prof_finish_kernel, dim3((B * H + 63) / 64), dim3(64), 0, s, ma.errp, B * H, pl.chunks, P,
-                       err, choice);
+    hipLaunchKernelGGL(prof_finish_kernel, dim3(B * H), dim3(256), 0, s, ma.errp, R, P, err, choice);
     return launch_status("vsa_profile_heads (finish)");
 }
