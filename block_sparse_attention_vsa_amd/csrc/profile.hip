@@ -9,14 +9,14 @@
 //  1. bits: for each candidate p and sampled row r, one bit per natural key n,
 //     set iff M_p[L_p(r) / bs][L_p(n) / bs] != 0, where L_p is the identity
 //     (mask stated in natural order) or the frame-major map (n -> s*T + t).
-//  2. main, in passes of two output slots (dense and candidate 0, then the
-//     next candidates): workgroups of 4 waves x 32 sampled rows walk a
-//     contiguous range of 64-key sub-tiles (split-K over keys, so that a few
-//     hundred rows still fill the chip), with K and V streamed into
-//     double-buffered LDS by DMA. Per sub-tile the scores S^T come from MFMA once
-//     per pass; each slot masks them with its bits, keeps its own online softmax
-//     (max, sum) and accumulates its own O^T. Each (slot, row, split) writes a
-//     partial record (m, l, O).
+//  2. main, one pass per output slot (dense, then each candidate; a single set
+//     of accumulators keeps 2 waves per SIMD without register spills):
+//     workgroups of 4 waves x 32 sampled rows walk a contiguous range of 64-key
+//     sub-tiles (split-K over keys, so that a few hundred rows still fill the
+//     chip), with K and V streamed into double-buffered LDS by DMA and the
+//     slot's bit words fetched one sub-tile ahead. Per sub-tile the scores S^T
+//     come from MFMA, the bits mask them, an online softmax (max, sum) runs and
+//     O^T accumulates. Each (slot, row, split) writes a partial record (m, l, O).
 //  3. merge: one workgroup per (b, h, sampled row) combines the partial records
 //     in split order (exact log-sum-exp rescaling), normalises every slot and
 //     sums each candidate's squared difference to the dense output.
@@ -32,8 +32,8 @@ namespace vsa {
 
 constexpr int kProfRows = 128;        // sampled rows per workgroup (4 waves x 32)
 constexpr int kProfMaxP = 4;
-constexpr int kProfTargetWG = 512;
-constexpr int kProfMaxSlots = 2;      // accumulator sets per pass (more would spill registers)
+constexpr int kProfTargetWG = 512;    // 256 CUs x 2 resident workgroups
+constexpr int kProfMaxSlots = 1;      // accumulator sets per pass: one keeps 2 waves per SIMD without spills
 
 struct ProfPlan {
     int nsub, RT, S, TPS, words;
@@ -48,7 +48,8 @@ static ProfPlan prof_plan(int B, int H, int64_t N, int D, int R, int P) {
     p.nsub = (int)((N + kSubKeys - 1) / kSubKeys);
     p.RT = (R + kProfRows - 1) / kProfRows;
     int64_t per = (int64_t)p.RT * B * H;
-    int S = (int)std::min<int64_t>(32, std::max<int64_t>(1, (kProfTargetWG + per - 1) / per));
+    // as many key splits as keep the whole grid resident at once (2 workgroups per CU)
+    int S = (int)std::min<int64_t>(32, std::max<int64_t>(1, kProfTargetWG / per));
     S = std::min(S, p.nsub);
     p.TPS = (p.nsub + S - 1) / S;
     p.S = (p.nsub + p.TPS - 1) / p.TPS;
@@ -116,7 +117,7 @@ struct ProfArgs {
 };
 
 template <int NC>
-__global__ __launch_bounds__(256) void prof_main_kernel(ProfArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void prof_main_kernel(ProfArgs a) {
     constexpr int D = 128, KT = kSubKeys;
     constexpr float TAU = 8.f;
     __shared__ __attribute__((aligned(1024))) uint8_t tiles[2][2][kSubBytes];
@@ -147,12 +148,35 @@ __global__ __launch_bounds__(256) void prof_main_kernel(ProfArgs a) {
         const int64_t row0 = head_off + (int64_t)t * KT * D;
         dma_kv_subtile<4>(tiles[stage][0], tiles[stage][1], a.k + row0, a.v + row0, vs, lane, w);
     };
-    if (t0 < t1) issue(t0, 0);
+    // candidate bit words of this lane's row, fetched one sub-tile ahead
+    auto load_bits = [&](int t, uint32_t (&wb)[NC][2]) {
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            const int cand = a.slot_cand[c];
+#pragma unroll
+            for (int st = 0; st < 2; ++st)
+                wb[c][st] = (cand < 0) ? 0xffffffffu
+                          : (row_ok ? a.bits[((int64_t)cand * a.R + ri) * a.words + 2 * t + st] : 0u);
+        }
+    };
+    uint32_t bits_cur[NC][2], bits_next[NC][2];
+    if (t0 < t1) {
+        issue(t0, 0);
+        load_bits(t0, bits_next);
+    }
     for (int t = t0; t < t1; ++t) {
         const int stage = (t - t0) & 1;
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
-        if (t + 1 < t1) issue(t + 1, stage ^ 1);
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            bits_cur[c][0] = bits_next[c][0];
+            bits_cur[c][1] = bits_next[c][1];
+        }
+        if (t + 1 < t1) {
+            issue(t + 1, stage ^ 1);
+            load_bits(t + 1, bits_next);
+        }
         if (!wave_active) continue;
         const int vs = min(KT, a.N - t * KT);
         f32x16 s[2];
@@ -167,13 +191,7 @@ __global__ __launch_bounds__(256) void prof_main_kernel(ProfArgs a) {
         const uint8_t* vt = tiles[stage][1];
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
-            const int cand = a.slot_cand[c];
-            uint32_t wbits[2] = {0xffffffffu, 0xffffffffu};
-            if (cand >= 0) {
-#pragma unroll
-                for (int st = 0; st < 2; ++st)
-                    wbits[st] = row_ok ? a.bits[((int64_t)cand * a.R + ri) * a.words + 2 * t + st] : 0u;
-            }
+            const uint32_t wbits[2] = {bits_cur[c][0], bits_cur[c][1]};
             float mx = -INFINITY;
 #pragma unroll
             for (int st = 0; st < 2; ++st)
@@ -361,7 +379,7 @@ extern "C" int vsa_profile_heads(const void* q, const void* k, const void* v, in
     pa.BH = B * H; pa.rec = pl.rec;
     pa.scale_log2 = (float)((double)scale * 1.4426950408889634);
     dim3 grid(pl.S, pl.RT, B * H);
-    // output slots 0 (dense) .. P in passes of up to two accumulator sets
+    // output slots 0 (dense) .. P, one accumulator set per pass
     for (int first = 0; first <= P; first += kProfMaxSlots) {
         const int nc = std::min(kProfMaxSlots, P + 1 - first);
         for (int c = 0; c < kProfMaxSlots; ++c) {
@@ -369,8 +387,8 @@ extern "C" int vsa_profile_heads(const void* q, const void* k, const void* v, in
             pa.slot_out[c] = slot;
             pa.slot_cand[c] = slot - 1;
         }
-        if (nc == 2) hipLaunchKernelGGL(prof_main_kernel<2>, grid, dim3(256), 0, s, pa);
-        else hipLaunchKernelGGL(prof_main_kernel<1>, grid, dim3(256), 0, s, pa);
+        (void)nc;
+        hipLaunchKernelGGL(prof_main_kernel<1>, grid, dim3(256), 0, s, pa);
         st = launch_status("vsa_profile_heads (main)");
         if (st) return st;
     }

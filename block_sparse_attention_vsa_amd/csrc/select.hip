@@ -5,14 +5,18 @@
 // by top-k cube selection, next to local attention; Sparse VideoGen2 page,
 // Abstract: top-p dynamic budget control.
 //
-// Per row (256 threads, row held in LDS):
-//  1. row max and Z = sum exp(s - max) by fixed-order tree reductions (fp32);
-//  2. a 64-bit key per block: [forced:1][order-preserving score bits:32]
-//     [~index:31], so one descending bitonic sort ranks forced blocks first,
-//     then by score, then by lower index;
-//  3. top-p: inclusive scan of exp(s - max) / Z over the ranked non-forced
-//     candidates (per-thread serial segments + a scan of the segment totals);
-//  4. kept blocks are flagged and compacted in ascending index order.
+// Each block gets a unique 64-bit rank key [forced:1][order-preserving score
+// bits:32][0x7fffffff - index:31]: larger key = better rank (forced first, then
+// higher score, then lower index). Per row (256 threads, row state in LDS):
+//  1. K = min(k_max, nkb): an MSB-first radix select (8-bit digits, histogram
+//     with integer LDS atomics, wave-level scans) finds the K-th largest key T;
+//     the K best blocks are exactly the keys >= T.
+//  2. Without top-p (or when forced blocks fill the cap) those K blocks are kept.
+//     With top-p, the K winners are sorted (bitonic, in LDS) and the softmax mass
+//     of the ranked non-forced candidates is accumulated in rank order until it
+//     reaches top_p; softmax is over all nkb scores of the row (fp32, Z summed in
+//     a fixed tree order).
+//  3. Kept blocks are written in ascending index order.
 #include <math.h>
 
 #include "vsa_internal.h"
@@ -25,7 +29,14 @@ __device__ __forceinline__ uint32_t order_bits(float f) {
     uint32_t u = __float_as_uint(f);
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
+__device__ __forceinline__ float score_of_key(uint64_t key) {
+    uint32_t o = (uint32_t)(key >> 31);
+    uint32_t u = (o & 0x80000000u) ? (o & 0x7fffffffu) : ~o;
+    return __uint_as_float(u);
+}
+__device__ __forceinline__ int index_of_key(uint64_t key) { return 0x7fffffff - (int)(key & 0x7fffffffull); }
 
+// Fixed-order block reduction over 256 threads.
 __device__ __forceinline__ float block_reduce(float v, float* red, bool is_max) {
     const int tid = threadIdx.x;
     red[tid] = v;
@@ -39,114 +50,138 @@ __device__ __forceinline__ float block_reduce(float v, float* red, bool is_max) 
     return r;
 }
 
-__global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ scores, int nqb, int nkb, int P2,
+// Inclusive scan of one value per thread over 256 threads (wave scans + totals).
+__device__ __forceinline__ uint32_t block_scan(uint32_t v, uint32_t* wave_tot) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        uint32_t t = __shfl_up(v, off);
+        if (lane >= off) v += t;
+    }
+    if (lane == 63) wave_tot[w] = v;
+    __syncthreads();
+    for (int i = 0; i < w; ++i) v += wave_tot[i];
+    __syncthreads();
+    return v;
+}
+
+__global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ scores, int nqb, int nkb, int P2K,
                                                      const uint8_t* __restrict__ forced, int k_max, float top_p,
                                                      int32_t* __restrict__ kv_idx, int32_t* __restrict__ kv_cnt) {
-    __shared__ uint64_t keys[kSelMax];
-    __shared__ float srow[kSelMax];
+    extern __shared__ __attribute__((aligned(16))) uint8_t dyn[];
+    uint64_t* keys = reinterpret_cast<uint64_t*>(dyn);                 // [nkb]
+    uint64_t* tops = keys + nkb;                                       // [P2K]
+    uint8_t* keep = reinterpret_cast<uint8_t*>(tops + P2K);            // [nkb]
     __shared__ float red[256];
-    __shared__ int flag_cnt[4];
-    __shared__ float seg[256];
-    __shared__ int cut;
-    __shared__ uint8_t keep[kSelMax];
+    __shared__ uint32_t hist[256];
+    __shared__ uint32_t wave_tot[4];
+    __shared__ uint64_t sel_prefix;
+    __shared__ uint32_t sel_above, sel_bin;
+    __shared__ int n_keep_s, n_top_s;
+
     const int tid = threadIdx.x;
     const int64_t row = blockIdx.x;
     const int qb = (int)(row % nqb);
     const float* s = scores + row * (int64_t)nkb;
     const uint8_t* f = forced ? forced + (int64_t)qb * nkb : nullptr;
+    const bool use_p = top_p < 1.f;
 
     float mx = -INFINITY;
     int nf_local = 0;
-    for (int j = tid; j < P2; j += 256) {
-        if (j < nkb) {
-            float v = s[j];
-            bool fj = f && f[j];
-            srow[j] = v;
-            mx = fmaxf(mx, v);
-            nf_local += fj;
-            keys[j] = ((uint64_t)(fj ? 1u : 0u) << 63) | ((uint64_t)order_bits(v) << 31) |
-                      (uint64_t)(0x7fffffffu - (uint32_t)j);
-        } else {
-            keys[j] = 0ull;                  // padding sorts last
-        }
-        if (j < nkb) keep[j] = 0;
+    for (int j = tid; j < nkb; j += 256) {
+        const float v = s[j];
+        const bool fj = f && f[j];
+        mx = fmaxf(mx, v);
+        nf_local += fj;
+        keys[j] = ((uint64_t)(fj ? 1u : 0u) << 63) | ((uint64_t)order_bits(v) << 31) |
+                  (uint64_t)(0x7fffffffu - (uint32_t)j);
+        keep[j] = 0;
     }
-    mx = block_reduce(mx, red, true);
     const int nforced = (int)block_reduce((float)nf_local, red, false);
-    float z_local = 0.f;
-    for (int j = tid; j < nkb; j += 256) z_local += expf(srow[j] - mx);
-    const float Z = block_reduce(z_local, red, false);
+    const int K = min(k_max, nkb);
 
-    // ---- descending bitonic sort of keys[0, P2) ----------------------------
-    for (int size = 2; size <= P2; size <<= 1) {
-        for (int stride = size >> 1; stride > 0; stride >>= 1) {
-            for (int t = tid; t < P2 / 2; t += 256) {
-                int lo = 2 * t - (t & (stride - 1));
-                int hi = lo + stride;
-                bool desc = (lo & size) == 0;
-                uint64_t a = keys[lo], b = keys[hi];
-                if ((a < b) == desc) { keys[lo] = b; keys[hi] = a; }
-            }
-            __syncthreads();
+    // ---- 1. radix select of the K-th largest key -------------------------------
+    uint64_t prefix = 0, pmask = 0;
+    uint32_t krem = (uint32_t)K;
+    for (int shift = 56; shift >= 0; shift -= 8) {
+        hist[tid] = 0;
+        __syncthreads();
+        for (int j = tid; j < nkb; j += 256) {
+            const uint64_t key = keys[j];
+            if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
         }
+        __syncthreads();
+        // thread t looks at digit 255 - t (descending), cum = count of digits >= it
+        const uint32_t c = hist[255 - tid];
+        const uint32_t cum = block_scan(c, wave_tot);
+        if (cum >= krem && cum - c < krem) {
+            sel_prefix = prefix | ((uint64_t)(255 - tid) << shift);
+            sel_above = cum - c;
+            sel_bin = c;
+        }
+        __syncthreads();
+        prefix = sel_prefix;
+        pmask |= (uint64_t)0xff << shift;
+        krem -= sel_above;
+        if (sel_bin == krem) break;      // every key in this bin is taken: the prefix is the threshold
+        __syncthreads();
     }
+    const uint64_t T = prefix;          // keys >= T are exactly the K best (low bits of T are zero past the stop)
 
-    // ---- how many ranked entries to keep -----------------------------------
-    int n_keep;
-    if (nforced >= k_max) {
-        n_keep = k_max;
+    // ---- 2. how many of the ranked winners to keep -----------------------------
+    if (!use_p || nforced >= k_max) {
+        for (int j = tid; j < nkb; j += 256) keep[j] = keys[j] >= T;
     } else {
-        const int n_cand = nkb - nforced;
-        const int room = k_max - nforced;
-        int r = n_cand;
-        if (top_p < 1.f && n_cand > 0) {
-            // inclusive scan of candidate probabilities in rank order
-            const int per = (n_cand + 255) / 256;
-            const int beg = min(tid * per, n_cand), end = min(beg + per, n_cand);
-            float acc = 0.f;
-            for (int i = beg; i < end; ++i) {
-                int j = 0x7fffffff - (int)(keys[nforced + i] & 0x7fffffffull);
-                acc += expf(srow[j] - mx) / Z;
+        mx = block_reduce(mx, red, true);
+        float z_local = 0.f;
+        for (int j = tid; j < nkb; j += 256) z_local += expf(s[j] - mx);
+        const float Z = block_reduce(z_local, red, false);
+        // compact the K winners, then sort them descending
+        if (tid == 0) n_top_s = 0;
+        for (int i = tid; i < P2K; i += 256) tops[i] = 0ull;
+        __syncthreads();
+        for (int j = tid; j < nkb; j += 256)
+            if (keys[j] >= T) tops[atomicAdd(&n_top_s, 1)] = keys[j];   // order fixed by the sort below
+        __syncthreads();
+        for (int size = 2; size <= P2K; size <<= 1) {
+            for (int stride = size >> 1; stride > 0; stride >>= 1) {
+                for (int t = tid; t < P2K / 2; t += 256) {
+                    const int lo = 2 * t - (t & (stride - 1));
+                    const int hi = lo + stride;
+                    const bool desc = (lo & size) == 0;
+                    const uint64_t a = tops[lo], b = tops[hi];
+                    if ((a < b) == desc) { tops[lo] = b; tops[hi] = a; }
+                }
+                __syncthreads();
             }
-            seg[tid] = acc;
-            if (tid == 0) cut = n_cand;
-            __syncthreads();
-            if (tid == 0) {                   // exclusive prefix of segment totals, in order
-                float run = 0.f;
-                for (int i = 0; i < 256; ++i) { float t = seg[i]; seg[i] = run; run += t; }
-            }
-            __syncthreads();
-            float run = seg[tid];
-            int first = n_cand;
-            for (int i = beg; i < end; ++i) {
-                int j = 0x7fffffff - (int)(keys[nforced + i] & 0x7fffffffull);
-                run += expf(srow[j] - mx) / Z;
-                if (run >= top_p) { first = i; break; }
-            }
-            if (first < n_cand) atomicMin(&cut, first);   // integer min: order-independent
-            __syncthreads();
-            r = max(min(cut + 1, n_cand), 1);
         }
-        n_keep = nforced + min(r, room);
-    }
-    for (int i = tid; i < n_keep; i += 256) {
-        int j = 0x7fffffff - (int)(keys[i] & 0x7fffffffull);
-        keep[j] = 1;
+        if (tid == 0) {
+            // forced blocks (all of them, since nforced < k_max) lead the ranked list
+            float cum = 0.f;
+            int r = K - nforced;             // every ranked candidate that fits the cap
+            for (int i = nforced; i < K; ++i) {
+                cum += expf(score_of_key(tops[i]) - mx) / Z;
+                if (cum >= top_p) { r = i - nforced + 1; break; }
+            }
+            n_keep_s = nforced + r;
+        }
+        __syncthreads();
+        for (int i = tid; i < n_keep_s; i += 256) keep[index_of_key(tops[i])] = 1;
     }
     __syncthreads();
 
-    // ---- ascending compaction ---------------------------------------------
+    // ---- 3. ascending compaction ------------------------------------------------
     const int lane = tid & 63, w = tid >> 6;
     int32_t* out = kv_idx + row * (int64_t)k_max;
     int base = 0;
     for (int r0 = 0; r0 < nkb; r0 += 256) {
-        int j = r0 + tid;
-        bool kj = j < nkb && keep[j];
-        uint64_t bal = __ballot(kj);
-        if (lane == 0) flag_cnt[w] = __popcll(bal);
+        const int j = r0 + tid;
+        const bool kj = j < nkb && keep[j];
+        const uint64_t bal = __ballot(kj);
+        if (lane == 0) wave_tot[w] = __popcll(bal);
         __syncthreads();
         int before = 0, total = 0;
-        for (int i = 0; i < 4; ++i) { before += (i < w) ? flag_cnt[i] : 0; total += flag_cnt[i]; }
+        for (int i = 0; i < 4; ++i) { before += (i < w) ? (int)wave_tot[i] : 0; total += (int)wave_tot[i]; }
         if (kj) out[base + before + __popcll(bal & ((1ull << lane) - 1ull))] = j;
         base += total;
         __syncthreads();
@@ -167,10 +202,11 @@ extern "C" int vsa_select_topk(const float* scores, int B, int H, int nqb, int n
     if (!(top_p > 0.f) || !(top_p <= 1.f)) return fail(VSA_ERR_INVALID, "vsa_select_topk: top_p must be in (0, 1]");
     int64_t rows = (int64_t)B * H * nqb;
     if (rows >= (1ll << 31)) return fail(VSA_ERR_INVALID, "vsa_select_topk: too many rows");
-    int P2 = 2;
-    while (P2 < nkb) P2 <<= 1;
-    P2 = P2 < 512 ? 512 : P2;                  // every thread owns whole compare pairs
-    hipLaunchKernelGGL(select_kernel, dim3((unsigned)rows), dim3(256), 0, as_stream(stream), scores, nqb, nkb, P2,
+    int P2K = 512;                       // every thread owns whole compare pairs
+    while (P2K < k_max) P2K <<= 1;
+    if (top_p >= 1.f) P2K = 0;           // no sort without top-p
+    const size_t shm = (size_t)nkb * 8 + (size_t)P2K * 8 + (size_t)((nkb + 15) & ~15);
+    hipLaunchKernelGGL(select_kernel, dim3((unsigned)rows), dim3(256), shm, as_stream(stream), scores, nqb, nkb, P2K,
                        forced, k_max, top_p, kv_idx, kv_cnt);
     return launch_status("vsa_select_topk");
 }
