@@ -214,6 +214,11 @@ __global__ __launch_bounds__(BS * 2) void attn_fwd_bf16_kernel(AttnArgs a) {
 //    the current one is computed. Each lane picks the global 16-byte chunk that
 //    belongs at its LDS slot, which realises an XOR swizzle of the chunks:
 //    K row r keeps chunk c at slot c ^ (r & 15), V row r at slot c ^ 4 (r & 3).
+//  * The two stages are distinct LDS objects and the loop is unrolled by two, so
+//    the compiler can see that a DMA into one stage never aliases reads of the
+//    other; the list entries and valid lengths are read through the constant
+//    address space (scalar loads), so waiting for them never waits for the DMA.
+//    Together this keeps the prefetch asynchronous.
 //  * K is read with ds_read_b128 (16 consecutive keys hit 16 distinct slots).
 //  * V stays row-major; the MFMA operand V^T comes from ds_read_b64_tr_b16: in a
 //    16-lane group, lanes 4j..4j+3 point at 16 consecutive channels of key j, and
@@ -222,14 +227,27 @@ __global__ __launch_bounds__(BS * 2) void attn_fwd_bf16_kernel(AttnArgs a) {
 //  * Softmax keeps a running offset m per query that only moves when a tile's
 //    max exceeds it by more than 8 (log2 units), so O is rarely rescaled; p stays
 //    below 2^8 and the final O / l is unchanged.
+__device__ __forceinline__ int32_t ld_const(const int32_t* p, int64_t i) {
+    return ((const __attribute__((address_space(4))) int32_t*)p)[i];
+}
+__device__ __forceinline__ int block_valid_c(const int32_t* blk_len, int b, int BS, int N) {
+    int exist = min(BS, N - b * BS);
+    return blk_len ? min(ld_const(blk_len, b), exist) : exist;
+}
+
 template <int BS>
 __global__ __launch_bounds__(BS * 2) __attribute__((amdgpu_waves_per_eu(2))) void attn_fwd_bf16_d128_kernel(AttnArgs a) {
     constexpr int D = 128, KT = 64;
     constexpr int WAVES = BS / 32, THREADS = WAVES * 64, SUB = BS / KT;
-    constexpr int TILE = kSubBytes;                  // bytes of one K or V sub-tile
     constexpr float TAU = 8.f;
 
-    __shared__ __attribute__((aligned(1024))) uint8_t tiles[2][2][TILE];   // [stage][K, V]
+    // 128-row blocks: two stages (2 workgroups per CU); 64-row blocks: one stage,
+    // so that 4 workgroups fit a CU and overlap each other's loads instead
+    constexpr bool TWO_STAGES = (BS == 128);
+    __shared__ __attribute__((aligned(1024))) uint8_t k0[kSubBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t v0[kSubBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t k1[TWO_STAGES ? kSubBytes : 16];
+    __shared__ __attribute__((aligned(1024))) uint8_t v1[TWO_STAGES ? kSubBytes : 16];
     __shared__ int16_t list_lds[kMaxMaskBlocks];
     __shared__ int wave_cnt[WAVES];
 
@@ -239,7 +257,7 @@ __global__ __launch_bounds__(BS * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
     const int item = xcd_remap(blockIdx.x, a.num_items);
     const int bh = item / nqb, qb = item - bh * nqb;
     const int64_t head_off = (int64_t)bh * a.N * D;
-    const int valid_q = block_valid(a.blk_len, qb, BS, a.N);
+    const int valid_q = block_valid_c(a.blk_len, qb, BS, a.N);
     const bool wave_active = 32 * w < valid_q;
 
     int cnt;
@@ -247,26 +265,22 @@ __global__ __launch_bounds__(BS * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
     if (a.mask) {
         cnt = compact_mask_row<THREADS>(a.mask + (int64_t)item * nkb, nkb, list_lds, wave_cnt);
     } else {
-        cnt = min(a.kv_cnt[item], a.max_kv);
+        cnt = min(ld_const(a.kv_cnt, item), a.max_kv);
         list_g = a.kv_idx + (int64_t)item * a.max_kv;
     }
-    auto block_of = [&](int it) -> int {
-        int kb = a.mask ? (int)list_lds[it] : list_g[it];
-        return ((unsigned)kb < (unsigned)nkb) ? kb : -1;    // malformed entries are skipped
-    };
     // valid keys of sub-tile i (0 when it holds none, or its block entry is malformed)
     auto sub_valid = [&](int i, int& kb) -> int {
-        kb = block_of(i / SUB);
-        if (kb < 0) return 0;
-        int v = block_valid(a.blk_len, kb, BS, a.N) - (i % SUB) * KT;
+        kb = a.mask ? (int)list_lds[i / SUB] : ld_const(list_g, i / SUB);
+        if ((unsigned)kb >= (unsigned)nkb) return 0;
+        int v = block_valid_c(a.blk_len, kb, BS, a.N) - (i % SUB) * KT;
         return v < 0 ? 0 : (v > KT ? KT : v);
     };
-    auto issue = [&](int i, int stage) {
+    auto issue = [&](int i, uint8_t* kd, uint8_t* vd) {
         int kb;
         const int vs = sub_valid(i, kb);
         if (vs == 0) return;
         const int64_t row0 = head_off + ((int64_t)kb * BS + (i % SUB) * KT) * D;
-        dma_kv_subtile<WAVES>(tiles[stage][0], tiles[stage][1], a.k + row0, a.v + row0, vs, lane, w);
+        dma_kv_subtile<WAVES>(kd, vd, a.k + row0, a.v + row0, vs, lane, w);
     };
 
     const int q_local = 32 * w + l32;
@@ -280,19 +294,10 @@ __global__ __launch_bounds__(BS * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
     for (int dt = 0; dt < D / 32; ++dt) o_acc[dt] = f32x16{};
     float m_run = -INFINITY, l_run = 0.f;
 
-    const int n_sub = cnt * SUB;
-    if (n_sub > 0) issue(0, 0);
-    for (int i = 0; i < n_sub; ++i) {
-        const int stage = i & 1;
-        __builtin_amdgcn_s_waitcnt(0);          // this thread's copies of sub-tile i have landed
-        __syncthreads();                        // ... and everyone's; stage ^ 1 is free again
-        if (i + 1 < n_sub) issue(i + 1, stage ^ 1);
+    auto compute = [&](int i, const uint8_t* kt, const uint8_t* vt) {
         int kb;
         const int vs = sub_valid(i, kb);
-        if (!wave_active || vs == 0) continue;
-        const uint8_t* kt = tiles[stage][0];
-        const uint8_t* vt = tiles[stage][1];
-
+        if (!wave_active || vs == 0) return;
         // ---- S^T = K Q^T (2 x 32 keys) ----------------------------------------
         f32x16 s[2];
         sub_scores(s, kt, qf, l32, half);
@@ -315,7 +320,7 @@ __global__ __launch_bounds__(BS * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
         const float m_new = upd ? m_tile : m_run;
         const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
         if (__ballot(upd)) {
-            const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);          // 1 where the offset stays
+            const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);   // 1 where the offset stays
             l_run *= alpha;
 #pragma unroll
             for (int dt = 0; dt < D / 32; ++dt)
@@ -336,7 +341,6 @@ __global__ __launch_bounds__(BS * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
                 pf[st][x >> 3][x & 7] = (__bf16)p;
             }
         l_run += (ps[0] + ps[1]) + (ps[2] + ps[3]);
-
         // ---- O^T += V^T P^T, V^T through transposing LDS reads -------------------
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt)
@@ -346,6 +350,31 @@ __global__ __launch_bounds__(BS * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
                 for (int g = 0; g < 2; ++g)
                     o_acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sub_vt_operand(vt, dt, st, g, lane),
                                                                         pf[st][g], o_acc[dt], 0, 0, 0);
+    };
+
+    const int n_sub = cnt * SUB;
+    if (n_sub > 0) issue(0, k0, v0);
+    if constexpr (TWO_STAGES) {
+        for (int i = 0; i < n_sub; i += 2) {
+            __builtin_amdgcn_s_waitcnt(0);          // this thread's copies of sub-tile i have landed
+            __syncthreads();                        // ... and everyone's; stage 1 is free again
+            if (i + 1 < n_sub) issue(i + 1, k1, v1);
+            compute(i, k0, v0);
+            if (i + 1 < n_sub) {
+                __builtin_amdgcn_s_waitcnt(0);
+                __syncthreads();
+                if (i + 2 < n_sub) issue(i + 2, k0, v0);
+                compute(i + 1, k1, v1);
+            }
+        }
+    } else {
+        for (int i = 0; i < n_sub; ++i) {
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+            compute(i, k0, v0);
+            __syncthreads();                        // stage free before the next copy
+            if (i + 1 < n_sub) issue(i + 1, k0, v0);
+        }
     }
 
     const float l_tot = pair_sum(l_run);

@@ -120,7 +120,12 @@ template <int NC>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void prof_main_kernel(ProfArgs a) {
     constexpr int D = 128, KT = kSubKeys;
     constexpr float TAU = 8.f;
-    __shared__ __attribute__((aligned(1024))) uint8_t tiles[2][2][kSubBytes];
+    // two stages as distinct LDS objects, loop unrolled by two: a DMA into one
+    // stage is then provably disjoint from reads of the other
+    __shared__ __attribute__((aligned(1024))) uint8_t k0[kSubBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t v0[kSubBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t k1[kSubBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t v1[kSubBytes];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int l32 = lane & 31, half = lane >> 5;
     const int split = blockIdx.x, rt = blockIdx.y, bh = blockIdx.z;
@@ -143,10 +148,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
         for (int dt = 0; dt < D / 32; ++dt) o[c][dt] = f32x16{};
     }
     const int t0 = split * a.TPS, t1 = min(t0 + a.TPS, a.nsub);
-    auto issue = [&](int t, int stage) {
+    auto issue = [&](int t, uint8_t* kd, uint8_t* vd) {
         const int vs = min(KT, a.N - t * KT);
         const int64_t row0 = head_off + (int64_t)t * KT * D;
-        dma_kv_subtile<4>(tiles[stage][0], tiles[stage][1], a.k + row0, a.v + row0, vs, lane, w);
+        dma_kv_subtile<4>(kd, vd, a.k + row0, a.v + row0, vs, lane, w);
     };
     // candidate bit words of this lane's row, fetched one sub-tile ahead
     auto load_bits = [&](int t, uint32_t (&wb)[NC][2]) {
@@ -160,27 +165,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
         }
     };
     uint32_t bits_cur[NC][2], bits_next[NC][2];
-    if (t0 < t1) {
-        issue(t0, 0);
-        load_bits(t0, bits_next);
-    }
-    for (int t = t0; t < t1; ++t) {
-        const int stage = (t - t0) & 1;
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-#pragma unroll
-        for (int c = 0; c < NC; ++c) {
-            bits_cur[c][0] = bits_next[c][0];
-            bits_cur[c][1] = bits_next[c][1];
-        }
-        if (t + 1 < t1) {
-            issue(t + 1, stage ^ 1);
-            load_bits(t + 1, bits_next);
-        }
-        if (!wave_active) continue;
+    auto compute = [&](int t, const uint8_t* kt, const uint8_t* vt) {
+        if (!wave_active) return;
         const int vs = min(KT, a.N - t * KT);
         f32x16 s[2];
-        sub_scores(s, tiles[stage][0], qf, l32, half);
+        sub_scores(s, kt, qf, l32, half);
         if (vs < KT) {
 #pragma unroll
             for (int st = 0; st < 2; ++st)
@@ -188,7 +177,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
                 for (int x = 0; x < 16; ++x)
                     if (acc_key(st, x, half) >= vs) s[st][x] = -INFINITY;
         }
-        const uint8_t* vt = tiles[stage][1];
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
             const uint32_t wbits[2] = {bits_cur[c][0], bits_cur[c][1]};
@@ -232,6 +220,37 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
                     for (int g = 0; g < 2; ++g)
                         o[c][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sub_vt_operand(vt, dt, st, g, lane),
                                                                            pf[st][g], o[c][dt], 0, 0, 0);
+        }
+    };
+    auto rotate = [&]() {
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            bits_cur[c][0] = bits_next[c][0];
+            bits_cur[c][1] = bits_next[c][1];
+        }
+    };
+    if (t0 < t1) {
+        issue(t0, k0, v0);
+        load_bits(t0, bits_next);
+    }
+    for (int t = t0; t < t1; t += 2) {
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        rotate();
+        if (t + 1 < t1) {
+            issue(t + 1, k1, v1);
+            load_bits(t + 1, bits_next);
+        }
+        compute(t, k0, v0);
+        if (t + 1 < t1) {
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+            rotate();
+            if (t + 2 < t1) {
+                issue(t + 2, k0, v0);
+                load_bits(t + 2, bits_next);
+            }
+            compute(t + 1, k1, v1);
         }
     }
     if (!wave_active) return;
