@@ -315,7 +315,7 @@ def main():
     if not args.no_extra:
         extra = extra_layers(torch, V, PL, T)
 
-    digest = source_digest("attn_fwd.hip", "vsa_internal.h")
+    digest = source_digest("attn_fwd.hip", "mfma_tile.h", "vsa_internal.h")
     traffic = stored_traffic("attn_fwd_bf16_d128_kernel<128>/wan480_svg", digest)
     roofline = {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
