@@ -208,12 +208,14 @@ __global__ __launch_bounds__(BS * 2) void attn_fwd_bf16_kernel(AttnArgs a) {
 //
 // Per workgroup one query block (BS rows, BS/32 waves of 32 rows); the kept key
 // blocks are walked in 64-key sub-tiles, double-buffered in LDS:
-//  * K and V sub-tiles go from HBM straight into LDS with global_load_lds_dwordx4
-//    (lane l of a wave instruction lands at base + 16 l), so no VGPRs or VALU
-//    instructions are spent staging tiles, and the next sub-tile streams in while
-//    the current one is computed. Each lane picks the global 16-byte chunk that
-//    belongs at its LDS slot, which realises an XOR swizzle of the chunks:
-//    K row r keeps chunk c at slot c ^ (r & 15), V row r at slot c ^ 4 (r & 3).
+//  * K and V sub-tiles go from HBM straight into LDS with buffer loads carrying
+//    the lds flag (lane l of a wave instruction lands at base + 16 l), so no
+//    VGPRs or VALU instructions are spent staging tiles, and the next sub-tile
+//    streams in while the current one is computed. Each lane picks the global
+//    16-byte chunk that belongs at its LDS slot, which realises an XOR swizzle of
+//    the chunks: K row r keeps chunk c at slot c ^ (r & 15), V row r at slot
+//    c ^ 4 (r & 3). Those per-lane offsets are fixed for the whole loop; the
+//    buffer descriptor spans one head, so rows past its end read as zeros.
 //  * The two stages are distinct LDS objects and the loop is unrolled by two, so
 //    the compiler can see that a DMA into one stage never aliases reads of the
 //    other; the list entries and valid lengths are read through the constant
@@ -275,12 +277,13 @@ __global__ __launch_bounds__(BS * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
         int v = block_valid_c(a.blk_len, kb, BS, a.N) - (i % SUB) * KT;
         return v < 0 ? 0 : (v > KT ? KT : v);
     };
+    const SubTileDma<WAVES> dma(lane, w);
+    const int head_bytes = a.N * D * 2;
     auto issue = [&](int i, uint8_t* kd, uint8_t* vd) {
         int kb;
         const int vs = sub_valid(i, kb);
         if (vs == 0) return;
-        const int64_t row0 = head_off + ((int64_t)kb * BS + (i % SUB) * KT) * D;
-        dma_kv_subtile<WAVES>(kd, vd, a.k + row0, a.v + row0, vs, lane, w);
+        dma.issue(kd, vd, a.k + head_off, a.v + head_off, head_bytes, kb * BS + (i % SUB) * KT, w);
     };
 
     const int q_local = 32 * w + l32;

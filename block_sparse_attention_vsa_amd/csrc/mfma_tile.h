@@ -155,34 +155,53 @@ __device__ __forceinline__ float pair_sum(float x) {
 
 
 // ---------------------------------------------------------------------------
-// 64-key sub-tiles for D = 128 staged by DMA (global_load_lds_dwordx4).
+// 64-key sub-tiles for D = 128 staged by DMA (buffer_load_dwordx4 ... lds).
 //
-// A wave instruction of global_load_lds_dwordx4 writes lane l's 16 bytes to LDS
-// base + 16 l, i.e. 1 KiB = 4 rows of 256 bytes. Lane l of instruction ins
-// covers row 4 ins + (l >> 4), LDS slot l & 15 of that row, and fetches the
-// global chunk that belongs there:
+// A wave instruction of a buffer load with the lds flag writes lane l's 16
+// bytes to LDS base + 16 l, i.e. 1 KiB = 4 rows of 256 bytes. Lane l of
+// instruction ins covers row 4 ins + (l >> 4), LDS slot l & 15 of that row, and
+// fetches the global chunk that belongs there:
 //   K: slot p of row r holds chunk p ^ (r & 15)  (16 keys of one chunk: 16 slots)
 //   V: slot p of row r holds chunk p ^ 4 (r & 3) (the transposing reads below hit
 //      every 16-byte slot of a 256-byte row exactly twice per wave)
-// Rows at or past `valid` re-read row valid - 1 (in bounds; masked later).
+// These per-lane byte offsets do not depend on the sub-tile, so they are
+// computed once; the sub-tile's base is a scalar offset. The buffer descriptor
+// covers exactly one head's rows, so rows past the head's end read as zeros
+// (masked later) without any per-row clamping.
 constexpr int kSubKeys = 64;
 constexpr int kSubBytes = kSubKeys * 128 * 2;   // one K or V sub-tile, D = 128
 
-template <int WAVES>
-__device__ __forceinline__ void dma_kv_subtile(uint8_t* k_dst, uint8_t* v_dst, const uint16_t* kg,
-                                               const uint16_t* vg, int valid, int lane, int w) {
-    constexpr int D = 128;
-    const int p = lane & 15;
-#pragma unroll
-    for (int ins = w; ins < kSubBytes / 1024; ins += WAVES) {
-        const int row = 4 * ins + (lane >> 4);
-        const int rr = row < valid ? row : valid - 1;
-        __builtin_amdgcn_global_load_lds(kg + (int64_t)rr * D + 8 * (p ^ (row & 15)),
-            (__attribute__((address_space(3))) void*)(k_dst + ins * 1024), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(vg + (int64_t)rr * D + 8 * (p ^ (4 * (row & 3))),
-            (__attribute__((address_space(3))) void*)(v_dst + ins * 1024), 16, 0, 0);
-    }
+__device__ __forceinline__ void dma16(const void* base, int nbytes, void* lds_dst, int voff, int soff) {
+    __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, nbytes,
+                                                                 0x00020000);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_dst, 16, voff, soff, 0,
+                                             0);
 }
+
+template <int WAVES>
+struct SubTileDma {
+    static constexpr int IPW = kSubBytes / 1024 / WAVES;   // wave instructions per tensor per sub-tile
+    int voff_k[IPW], voff_v[IPW];
+    __device__ __forceinline__ SubTileDma(int lane, int w) {
+#pragma unroll
+        for (int u = 0; u < IPW; ++u) {
+            const int row = 4 * (w + WAVES * u) + (lane >> 4), p = lane & 15;
+            voff_k[u] = row * 256 + ((p ^ (row & 15)) << 4);
+            voff_v[u] = row * 256 + ((p ^ (4 * (row & 3))) << 4);
+        }
+    }
+    // k_head / v_head: the head's first row; head_bytes: its extent; row0: first
+    // key row of the sub-tile inside the head
+    __device__ __forceinline__ void issue(uint8_t* k_dst, uint8_t* v_dst, const uint16_t* k_head,
+                                          const uint16_t* v_head, int head_bytes, int row0, int w) const {
+#pragma unroll
+        for (int u = 0; u < IPW; ++u) {
+            const int ins = w + WAVES * u;
+            dma16(k_head, head_bytes, k_dst + ins * 1024, voff_k[u], row0 * 256);
+            dma16(v_head, head_bytes, v_dst + ins * 1024, voff_v[u], row0 * 256);
+        }
+    }
+};
 
 // S^T for a 64-key sub-tile: s[st] holds keys 32 st + acc_key(0, x, half).
 __device__ __forceinline__ void sub_scores(f32x16 (&s)[2], const uint8_t* kt, const bf16x8 (&qf)[8], int l32,

@@ -148,10 +148,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
         for (int dt = 0; dt < D / 32; ++dt) o[c][dt] = f32x16{};
     }
     const int t0 = split * a.TPS, t1 = min(t0 + a.TPS, a.nsub);
+    const SubTileDma<4> dma(lane, w);
+    const int head_bytes = a.N * D * 2;
     auto issue = [&](int t, uint8_t* kd, uint8_t* vd) {
-        const int vs = min(KT, a.N - t * KT);
-        const int64_t row0 = head_off + (int64_t)t * KT * D;
-        dma_kv_subtile<4>(kd, vd, a.k + row0, a.v + row0, vs, lane, w);
+        dma.issue(kd, vd, a.k + head_off, a.v + head_off, head_bytes, t * KT, w);
     };
     // candidate bit words of this lane's row, fetched one sub-tile ahead
     auto load_bits = [&](int t, uint32_t (&wb)[NC][2]) {
