@@ -247,20 +247,15 @@ def main():
         e2 = T.ev()
         sel = ch[0].cpu().tolist()
         e3 = T.ev()
-        qm = V.vsa_permute(q, grid, V.VSA_PERM_FRAME_MAJOR, False, sel)
-        km = V.vsa_permute(k, grid, V.VSA_PERM_FRAME_MAJOR, False, sel)
-        vm = V.vsa_permute(v, grid, V.VSA_PERM_FRAME_MAJOR, False, sel)
-        e4 = T.ev()
         idx, cnt = V.vsa_mask_to_list(cand, head_mask_idx=sel, B=B)
+        e4 = T.ev()
+        # a3 + a7 + a8: the frame-major permutation of the temporal heads is done
+        # by the attention kernel's loads and stores
+        o = V.vsa_block_sparse_attn_fwd_permuted(q, k, v, grid, bs, head_fm=sel, kv_idx=idx, kv_cnt=cnt)
         e5 = T.ev()
-        om = V.vsa_block_sparse_attn_fwd(qm, km, vm, bs, kv_idx=idx, kv_cnt=cnt)
-        e6 = T.ev()
-        o = V.vsa_permute(om, grid, V.VSA_PERM_FRAME_MAJOR, True, sel)
-        e7 = T.ev()
         if timed:
             for key, a, b in (("a1_pattern_masks", e0, e1), ("a2_profile", e1, e2), ("choice_sync", e2, e3),
-                              ("a3_permute_qkv", e3, e4), ("a6_mask_to_list", e4, e5), ("a7_attention", e5, e6),
-                              ("a8_permute_o", e6, e7)):
+                              ("a6_mask_to_list", e3, e4), ("a3_a7_a8_attention_fused_permute", e4, e5)):
                 T.add(key, a, b)
         return o, sel, idx, cnt
 
@@ -275,7 +270,7 @@ def main():
     ms_step = wall * 1e3 / args.steps
 
     flops = kept_flops_from_lists(idx, cnt, N, bs, D)
-    attn_ms = T.mean_ms("a7_attention")
+    attn_ms = T.mean_ms("a3_a7_a8_attention_fused_permute")
     attn_tflops = flops / (attn_ms * 1e-3) / 1e12
     comp = {key: round(T.mean_ms(key), 4) for key in T.acc}
 
@@ -306,10 +301,22 @@ def main():
         print(f"bench.py: torch SDPA baseline failed: {ex}", file=sys.stderr)
     dense_ms = min(x for x in (dense_ours, dense_sdpa) if x is not None)
 
-    # permutation bandwidth (a3: 3 tensors, read + write of the moved heads)
     n_moved = sum(sel)
-    perm_bytes = 3 * 2 * B * n_moved * N * D * 2
-    perm_gbs = perm_bytes / (comp["a3_permute_qkv"] * 1e-3) / 1e9 if n_moved else None
+    # the standalone permutation kernel (a3 / a8 as separate calls), every head
+    # moved: read + write of one [B, H, N, D] tensor per call
+    all_heads = [1] * H
+    pdst = torch.empty_like(q)
+    for _ in range(2):
+        V.vsa_permute(q, grid, V.VSA_PERM_FRAME_MAJOR, False, all_heads, out=pdst)
+    torch.cuda.synchronize()
+    e0 = T.ev()
+    for _ in range(10):
+        V.vsa_permute(q, grid, V.VSA_PERM_FRAME_MAJOR, False, all_heads, out=pdst)
+    e1 = T.ev()
+    torch.cuda.synchronize()
+    perm_ms = e0.elapsed_time(e1) / 10
+    perm_gbs = 2 * q.numel() * q.element_size() / (perm_ms * 1e-3) / 1e9
+    del pdst
 
     extra = {}
     if not args.no_extra:
@@ -340,7 +347,7 @@ def main():
         "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "wan2.1-1.3B 480p layer, Sparse VideoGen step (profile 1% rows, spatial w=1 / "
-                               "temporal w=0 per head, frame-major permute, block-sparse attention)",
+                               "temporal w=0 per head, frame-major order of temporal heads folded into the attention kernel)",
                    "B": B, "H": H, "N": N, "D": D, "grid": list(grid), "block": bs,
                    "heads_temporal": int(n_moved), "kept_block_density": round(float(cnt.sum().item()) / (B * H * w.nb * w.nb), 4)},
         "pct_mfma_peak_step": round(100 * value / PEAK_BF16_TFLOPS, 2),
@@ -349,7 +356,9 @@ def main():
         "speedup_vs_dense_step": round(dense_ms / ms_step, 2),
         "dense_ms": {"ours_all_blocks": round(dense_ours, 3), "torch_sdpa": None if dense_sdpa is None else round(dense_sdpa, 3)},
         "components_ms": comp,
-        "permute_GBps": None if perm_gbs is None else round(perm_gbs, 1),
+        "permute_standalone": {"ms": round(perm_ms, 4), "GBps": round(perm_gbs, 1),
+                               "frac_of_hbm_peak": round(perm_gbs / 8000.0, 3),
+                               "what": "vsa_permute frame-major, all 12 heads of one [1,12,32760,128] bf16 tensor"},
         "extra_layers": extra,
         "roofline": roofline,
         "cpu_baseline": cpu,
@@ -362,6 +371,46 @@ def extra_layers(torch, V, PL, T):
     few runs with per-call events: the pooling/score and selection steps live here."""
     res = {}
     dev = torch.device("cuda:0")
+
+    # Wan 480p with a 6/6 head split (even heads spatial w=1, odd heads temporal
+    # w=0 in frame-major order): the fused kernel against the separate sequence
+    # permute x3 -> attention -> inverse permute.
+    w = WAN480
+    q, k, v = (torch.from_numpy(x).to(torch.bfloat16).to(dev) for x in make_qkv(w))
+    sel = [h % 2 for h in range(w.H)]
+    cand = PL.svg_masks(w.grid, w.bs, w.extra["w_spatial"], w.extra["w_temporal"], dev)
+    idx, cnt = V.vsa_mask_to_list(cand, head_mask_idx=sel, B=1)
+    FMK = V.VSA_PERM_FRAME_MAJOR
+    times = {}
+    for rep in range(4):
+        e = [T.ev()]
+        o_f = V.vsa_block_sparse_attn_fwd_permuted(q, k, v, w.grid, w.bs, head_fm=sel, kv_idx=idx, kv_cnt=cnt)
+        e.append(T.ev())
+        qm = V.vsa_permute(q, w.grid, FMK, False, sel)
+        km = V.vsa_permute(k, w.grid, FMK, False, sel)
+        vm = V.vsa_permute(v, w.grid, FMK, False, sel)
+        e.append(T.ev())
+        om = V.vsa_block_sparse_attn_fwd(qm, km, vm, w.bs, kv_idx=idx, kv_cnt=cnt)
+        e.append(T.ev())
+        o_s = V.vsa_permute(om, w.grid, FMK, True, sel)
+        e.append(T.ev())
+        torch.cuda.synchronize()
+        if rep:
+            for key, i in (("fused_attention", 0), ("separate_permute_qkv", 1), ("separate_attention", 2),
+                           ("separate_permute_o", 3)):
+                times.setdefault(key, []).append(e[i].elapsed_time(e[i + 1]))
+    if not torch.equal(o_f, o_s):
+        print("bench.py: fused and separate frame-major paths disagree", file=sys.stderr)
+    fl = kept_flops_from_lists(idx, cnt, w.N, w.bs, 128)
+    ms = {k_: round(float(np.mean(v_)), 4) for k_, v_ in times.items()}
+    res["svg_6_6_split_wan480"] = {"ms": ms, "kept_flops": fl,
+                                   "fused_attn_tflops": round(fl / (ms["fused_attention"] * 1e-3) / 1e12, 2),
+                                   "separate_total_ms": round(ms["separate_permute_qkv"] + ms["separate_attention"]
+                                                              + ms["separate_permute_o"], 4),
+                                   "bit_identical": bool(torch.equal(o_f, o_s))}
+    del q, k, v, qm, km, vm, om, o_f, o_s, cand
+    torch.cuda.empty_cache()
+
     w = WAN480_CUBE
     q, k, v = (torch.from_numpy(x).to(torch.bfloat16).to(dev) for x in make_qkv(w))
     n_cubes, k_max = PL.cube_budget(w.grid, w.extra["k_frac"])

@@ -57,6 +57,8 @@ _SIGNATURES = {
     "vsa_attn_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I]),
     "vsa_block_sparse_attn_fwd": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P,
                                        ctypes.POINTER(vsa_blocks), _F, _P, _SZ, _P]),
+    "vsa_block_sparse_attn_fwd_permuted": (_I, [_P, _P, _P, _P, _P, _I, _I, vsa_grid, _I, _I, _I, _P, _P,
+                                                ctypes.POINTER(vsa_blocks), _F, _P]),
     "vsa_check_block_list_host": (_I, [_P, _P, _I64, _I, _I]),
 }
 
@@ -318,6 +320,56 @@ def vsa_block_sparse_attn_fwd(q, k, v, bs: int, mask=None, kv_idx=None, kv_cnt=N
                                            _dtype_code(q), bs, _ptr(blk_len), ctypes.byref(blocks), scale,
                                            _ptr(workspace), 0 if workspace is None else workspace.numel(),
                                            _stream(q.device)), "vsa_block_sparse_attn_fwd")
+    return (out, lse) if return_lse else out
+
+
+def _blocks_arg(q, bs, mask, kv_idx, kv_cnt):
+    torch = _torch()
+    blocks = vsa_blocks()
+    if mask is not None:
+        _need(mask, "mask", torch.uint8)
+        blocks.mask = mask.data_ptr()
+    if kv_idx is not None:
+        _need(kv_idx, "kv_idx", torch.int32, 4)
+        _need(kv_cnt, "kv_cnt", torch.int32, 3)
+        blocks.kv_idx = kv_idx.data_ptr()
+        blocks.kv_cnt = kv_cnt.data_ptr()
+        blocks.max_kv = kv_idx.shape[-1]
+    return blocks
+
+
+def vsa_block_sparse_attn_fwd_permuted(q, k, v, grid, bs: int, head_fm=None, mask=None, kv_idx=None, kv_cnt=None,
+                                       blk_len=None, scale=None, return_lse=False, out=None, lse=None):
+    """Attention with the frame-major permutation of the heads in `head_fm`
+    (host sequence of H flags) folded into the kernel's loads and stores; q, k,
+    v and the result are in natural order."""
+    torch = _torch()
+    _need(q, "q", ndim=4)
+    _need(k, "k", q.dtype, 4)
+    _need(v, "v", q.dtype, 4)
+    B, H, N, D = q.shape
+    if k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must have the same shape")
+    if N != int(np.prod(grid)):
+        raise ValueError("N must equal T*Hh*W")
+    scale = default_scale(D) if scale is None else scale
+    if out is None:
+        out = torch.empty_like(q)
+    if return_lse and lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    blocks = _blocks_arg(q, bs, mask, kv_idx, kv_cnt)
+    if blk_len is not None:
+        _need(blk_len, "blk_len", torch.int32, 1)
+    hf = None
+    if head_fm is not None:
+        if len(head_fm) != H:
+            raise ValueError("head_fm needs one flag per head")
+        hf_arr = (ctypes.c_uint8 * H)(*[1 if x else 0 for x in head_fm])
+        hf = ctypes.cast(hf_arr, ctypes.c_void_p)
+    _check(lib().vsa_block_sparse_attn_fwd_permuted(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H,
+                                                    _grid(grid), D, _dtype_code(q), bs, hf, _ptr(blk_len),
+                                                    ctypes.byref(blocks), scale, _stream(q.device)),
+           "vsa_block_sparse_attn_fwd_permuted")
     return (out, lse) if return_lse else out
 
 

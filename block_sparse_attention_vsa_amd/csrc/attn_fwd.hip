@@ -44,7 +44,18 @@ struct AttnArgs {
     int32_t H, N, nb;
     int32_t num_items;
     float scale_log2;      // scale * log2(e)
+    // frame-major heads (D = 128 bf16 kernel only): rows are read and written
+    // through the map natural n = t*HW + s <-> permuted r = s*T + t
+    int32_t T, HW;
+    FastDiv div_T;
+    uint32_t fm_bits[32];  // bit h set: head h is in frame-major order; all zero otherwise
 };
+
+// Natural row of permuted row r (r < N) for a frame-major head.
+__device__ __forceinline__ int fm_natural(const AttnArgs& a, int r) {
+    const uint32_t s = a.div_T.div((uint32_t)r);
+    return (int)(((uint32_t)r - s * (uint32_t)a.T) * (uint32_t)a.HW + s);
+}
 
 __device__ __forceinline__ int xcd_remap(int bid, int G) {
     // Workgroup `bid` runs on XCD bid % 8; give each XCD a contiguous item range.
@@ -237,7 +248,7 @@ __device__ __forceinline__ int block_valid_c(const int32_t* blk_len, int b, int 
     return blk_len ? min(ld_const(blk_len, b), exist) : exist;
 }
 
-template <int BS>
+template <int BS, bool GATHER>
 __global__ __launch_bounds__(BS * 2) __attribute__((amdgpu_waves_per_eu(2))) void attn_fwd_bf16_d128_kernel(AttnArgs a) {
     constexpr int D = 128, KT = 64;
     constexpr int WAVES = BS / 32, THREADS = WAVES * 64, SUB = BS / KT;
@@ -261,6 +272,13 @@ __global__ __launch_bounds__(BS * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
     const int64_t head_off = (int64_t)bh * a.N * D;
     const int valid_q = block_valid_c(a.blk_len, qb, BS, a.N);
     const bool wave_active = 32 * w < valid_q;
+    // frame-major head (uniform over the workgroup); launches without any such
+    // head use the GATHER = false instance, which carries no code for it
+    bool fm = false;
+    if constexpr (GATHER) {
+        const int h = bh % a.H;
+        fm = (a.fm_bits[h >> 5] >> (h & 31)) & 1u;
+    }
 
     int cnt;
     const int32_t* list_g = nullptr;
@@ -283,14 +301,18 @@ __global__ __launch_bounds__(BS * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
         int kb;
         const int vs = sub_valid(i, kb);
         if (vs == 0) return;
-        dma.issue(kd, vd, a.k + head_off, a.v + head_off, head_bytes, kb * BS + (i % SUB) * KT, w);
+        const int row0 = kb * BS + (i % SUB) * KT;
+        if (fm) dma.issue_frame_major(kd, vd, a.k + head_off, a.v + head_off, head_bytes, row0, a.N, a.T, a.HW, a.div_T, lane, w);
+        else dma.issue(kd, vd, a.k + head_off, a.v + head_off, head_bytes, row0, w);
     };
 
     const int q_local = 32 * w + l32;
     const int q_row = qb * BS + q_local;
     const bool q_ok = q_local < valid_q;
+    // row of this query in memory (natural order)
+    const int q_mem = (fm && q_row < a.N) ? fm_natural(a, q_row) : q_row;
     bf16x8 qf[D / 16];
-    load_q_frag<D>(qf, a.q + head_off + (int64_t)q_row * D, q_ok, half);
+    load_q_frag<D>(qf, a.q + head_off + (int64_t)q_mem * D, q_ok, half);
 
     f32x16 o_acc[D / 32];
 #pragma unroll
@@ -384,7 +406,7 @@ __global__ __launch_bounds__(BS * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
     if (q_row < a.N) {
         const bool has = q_ok && l_tot > 0.f;
         const float inv = has ? 1.f / l_tot : 0.f;
-        uint16_t* orow = a.o + head_off + (int64_t)q_row * D;
+        uint16_t* orow = a.o + head_off + (int64_t)q_mem * D;
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
@@ -399,7 +421,7 @@ __global__ __launch_bounds__(BS * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
                 *reinterpret_cast<u32x2*>(orow + 32 * dt + 8 * jj + 4 * half) = pk;
             }
         if (a.lse && half == 0)
-            a.lse[(int64_t)bh * a.N + q_row] = has ? (m_run + log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
+            a.lse[(int64_t)bh * a.N + q_mem] = has ? (m_run + log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
     }
 }
 
@@ -497,39 +519,41 @@ extern "C" size_t vsa_attn_workspace_bytes(int B, int H, int N, int bs, int max_
     return 0;
 }
 
-extern "C" int vsa_block_sparse_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B,
-                                         int H, int N, int D, int dtype, int bs, const int32_t* blk_len,
-                                         const vsa_blocks* blocks, float scale, void* workspace, size_t ws_bytes,
-                                         void* stream) {
-    (void)workspace; (void)ws_bytes;
-    if (!q || !k || !v || !o) return fail(VSA_ERR_INVALID, "vsa_block_sparse_attn_fwd: null tensor");
+namespace {
+
+// Validates the arguments shared by both entry points and fills `a` (no
+// frame-major heads). Returns VSA_OK or the failure status.
+int prepare_attn(const char* fn, AttnArgs& a, const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                 int H, int N, int D, int dtype, int bs, const int32_t* blk_len, const vsa_blocks* blocks,
+                 float scale) {
+    if (!q || !k || !v || !o) return fail(VSA_ERR_INVALID, "%s: null tensor", fn);
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
-        return fail(VSA_ERR_INVALID, "vsa_block_sparse_attn_fwd: tensors must be 16-byte aligned");
-    if (B <= 0 || H <= 0 || N <= 0) return fail(VSA_ERR_INVALID, "vsa_block_sparse_attn_fwd: B, H, N must be positive");
-    if (!blocks) return fail(VSA_ERR_INVALID, "vsa_block_sparse_attn_fwd: null blocks");
+        return fail(VSA_ERR_INVALID, "%s: tensors must be 16-byte aligned", fn);
+    if (B <= 0 || H <= 0 || N <= 0) return fail(VSA_ERR_INVALID, "%s: B, H, N must be positive", fn);
+    if (!blocks) return fail(VSA_ERR_INVALID, "%s: null blocks", fn);
     const bool has_mask = blocks->mask != nullptr;
     const bool has_list = blocks->kv_idx != nullptr || blocks->kv_cnt != nullptr;
-    if (has_mask == has_list)
-        return fail(VSA_ERR_INVALID, "vsa_block_sparse_attn_fwd: give exactly one of mask or (kv_idx, kv_cnt)");
+    if (has_mask == has_list) return fail(VSA_ERR_INVALID, "%s: give exactly one of mask or (kv_idx, kv_cnt)", fn);
     if (has_list && (!blocks->kv_idx || !blocks->kv_cnt || blocks->max_kv <= 0))
-        return fail(VSA_ERR_INVALID, "vsa_block_sparse_attn_fwd: list form needs kv_idx, kv_cnt and max_kv > 0");
-    if (!(scale > 0.f) || !__builtin_isfinite(scale))
-        return fail(VSA_ERR_INVALID, "vsa_block_sparse_attn_fwd: scale must be positive and finite");
-    if (D != 64 && D != 128) return fail(VSA_ERR_UNSUPPORTED, "vsa_block_sparse_attn_fwd: D must be 64 or 128 (got %d)", D);
+        return fail(VSA_ERR_INVALID, "%s: list form needs kv_idx, kv_cnt and max_kv > 0", fn);
+    if (!(scale > 0.f) || !__builtin_isfinite(scale)) return fail(VSA_ERR_INVALID, "%s: scale must be positive and finite", fn);
+    if (D != 64 && D != 128) return fail(VSA_ERR_UNSUPPORTED, "%s: D must be 64 or 128 (got %d)", fn, D);
     if (dtype == VSA_BF16) {
-        if (bs != 64 && bs != 128) return fail(VSA_ERR_UNSUPPORTED, "vsa_block_sparse_attn_fwd: bf16 needs bs 64 or 128 (got %d)", bs);
+        if (bs != 64 && bs != 128) return fail(VSA_ERR_UNSUPPORTED, "%s: bf16 needs bs 64 or 128 (got %d)", fn, bs);
     } else if (dtype == VSA_F32) {
-        if (bs != 64) return fail(VSA_ERR_UNSUPPORTED, "vsa_block_sparse_attn_fwd: fp32 needs bs 64 (got %d)", bs);
+        if (bs != 64) return fail(VSA_ERR_UNSUPPORTED, "%s: fp32 needs bs 64 (got %d)", fn, bs);
     } else {
-        return fail(VSA_ERR_UNSUPPORTED, "vsa_block_sparse_attn_fwd: dtype %d not supported", dtype);
+        return fail(VSA_ERR_UNSUPPORTED, "%s: dtype %d not supported", fn, dtype);
     }
     const int64_t nb = (N + (int64_t)bs - 1) / bs;
     if (has_mask && nb > kMaxMaskBlocks)
-        return fail(VSA_ERR_UNSUPPORTED, "vsa_block_sparse_attn_fwd: mask form supports at most %d blocks per row (use the list form)", kMaxMaskBlocks);
+        return fail(VSA_ERR_UNSUPPORTED, "%s: mask form supports at most %d blocks per row (use the list form)", fn,
+                    kMaxMaskBlocks);
     const int64_t items = (int64_t)B * H * nb;
-    if (items >= (1ll << 31) || (int64_t)B * H * N * D >= (1ll << 40))
-        return fail(VSA_ERR_INVALID, "vsa_block_sparse_attn_fwd: problem too large");
-    AttnArgs a;
+    const int64_t elt = dtype == VSA_BF16 ? 2 : 4;
+    if (items >= (1ll << 31) || (int64_t)N * D * elt >= (1ll << 31) || (int64_t)B * H * N * D >= (1ll << 40))
+        return fail(VSA_ERR_INVALID, "%s: problem too large", fn);
+    a = AttnArgs{};
     a.q = static_cast<const uint16_t*>(q);
     a.k = static_cast<const uint16_t*>(k);
     a.v = static_cast<const uint16_t*>(v);
@@ -543,16 +567,65 @@ extern "C" int vsa_block_sparse_attn_fwd(const void* q, const void* k, const voi
     a.H = H; a.N = N; a.nb = (int32_t)nb;
     a.num_items = (int32_t)items;
     a.scale_log2 = (float)((double)scale * 1.4426950408889634);
-    hipStream_t s = as_stream(stream);
-    dim3 grid((unsigned)items);
+    a.T = 1; a.HW = N; a.div_T = FastDiv(1u);
+    return VSA_OK;
+}
+
+void launch_attn(const AttnArgs& a, int D, int dtype, int bs, hipStream_t s) {
+    dim3 grid((unsigned)a.num_items);
     if (dtype == VSA_BF16) {
-        if (D == 128 && bs == 128) hipLaunchKernelGGL((attn_fwd_bf16_d128_kernel<128>), grid, dim3(256), 0, s, a);
-        else if (D == 128 && bs == 64) hipLaunchKernelGGL((attn_fwd_bf16_d128_kernel<64>), grid, dim3(128), 0, s, a);
+        bool gather = false;
+        for (int i = 0; i < 32; ++i) gather |= a.fm_bits[i] != 0;
+        if (D == 128 && bs == 128) {
+            if (gather) hipLaunchKernelGGL((attn_fwd_bf16_d128_kernel<128, true>), grid, dim3(256), 0, s, a);
+            else hipLaunchKernelGGL((attn_fwd_bf16_d128_kernel<128, false>), grid, dim3(256), 0, s, a);
+        } else if (D == 128 && bs == 64) {
+            if (gather) hipLaunchKernelGGL((attn_fwd_bf16_d128_kernel<64, true>), grid, dim3(128), 0, s, a);
+            else hipLaunchKernelGGL((attn_fwd_bf16_d128_kernel<64, false>), grid, dim3(128), 0, s, a);
+        }
         else if (D == 64 && bs == 128) hipLaunchKernelGGL((attn_fwd_bf16_kernel<64, 128>), grid, dim3(256), 0, s, a);
         else hipLaunchKernelGGL((attn_fwd_bf16_kernel<64, 64>), grid, dim3(128), 0, s, a);
     } else {
         if (D == 64) hipLaunchKernelGGL((attn_fwd_f32_kernel<64>), grid, dim3(64), 0, s, a);
         else hipLaunchKernelGGL((attn_fwd_f32_kernel<128>), grid, dim3(64), 0, s, a);
     }
+}
+
+}  // namespace
+
+extern "C" int vsa_block_sparse_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                                         int H, int N, int D, int dtype, int bs, const int32_t* blk_len,
+                                         const vsa_blocks* blocks, float scale, void* workspace, size_t ws_bytes,
+                                         void* stream) {
+    (void)workspace; (void)ws_bytes;
+    AttnArgs a;
+    const int st = prepare_attn("vsa_block_sparse_attn_fwd", a, q, k, v, o, lse, B, H, N, D, dtype, bs, blk_len,
+                                blocks, scale);
+    if (st != VSA_OK) return st;
+    launch_attn(a, D, dtype, bs, as_stream(stream));
     return launch_status("vsa_block_sparse_attn_fwd");
+}
+
+extern "C" int vsa_block_sparse_attn_fwd_permuted(const void* q, const void* k, const void* v, void* o, float* lse,
+                                                  int B, int H, vsa_grid g, int D, int dtype, int bs,
+                                                  const uint8_t* head_fm, const int32_t* blk_len,
+                                                  const vsa_blocks* blocks, float scale, void* stream) {
+    const char* fn = "vsa_block_sparse_attn_fwd_permuted";
+    if (g.T <= 0 || g.Hh <= 0 || g.W <= 0) return fail(VSA_ERR_INVALID, "%s: grid extents must be positive", fn);
+    const int64_t N64 = (int64_t)g.T * g.Hh * g.W;
+    if (N64 >= (1ll << 31)) return fail(VSA_ERR_INVALID, "%s: grid too large", fn);
+    if (H > 1024) return fail(VSA_ERR_UNSUPPORTED, "%s: at most 1024 heads", fn);
+    AttnArgs a;
+    const int st = prepare_attn(fn, a, q, k, v, o, lse, B, H, (int)N64, D, dtype, bs, blk_len, blocks, scale);
+    if (st != VSA_OK) return st;
+    if (dtype != VSA_BF16 || D != 128)
+        return fail(VSA_ERR_UNSUPPORTED, "%s: frame-major heads need bf16 with D = 128", fn);
+    a.T = g.T;
+    a.HW = g.Hh * g.W;
+    a.div_T = FastDiv((uint32_t)g.T);
+    if (head_fm)
+        for (int h = 0; h < H; ++h)
+            if (head_fm[h]) a.fm_bits[h >> 5] |= 1u << (h & 31);
+    launch_attn(a, D, dtype, bs, as_stream(stream));
+    return launch_status(fn);
 }

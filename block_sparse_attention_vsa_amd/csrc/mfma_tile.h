@@ -181,7 +181,7 @@ __device__ __forceinline__ void dma16(const void* base, int nbytes, void* lds_ds
 template <int WAVES>
 struct SubTileDma {
     static constexpr int IPW = kSubBytes / 1024 / WAVES;   // wave instructions per tensor per sub-tile
-    int voff_k[IPW], voff_v[IPW];
+    int voff_k[IPW], voff_v[IPW];   // byte offset of this lane's chunk inside the sub-tile
     __device__ __forceinline__ SubTileDma(int lane, int w) {
 #pragma unroll
         for (int u = 0; u < IPW; ++u) {
@@ -190,15 +190,32 @@ struct SubTileDma {
             voff_v[u] = row * 256 + ((p ^ (4 * (row & 3))) << 4);
         }
     }
-    // k_head / v_head: the head's first row; head_bytes: its extent; row0: first
-    // key row of the sub-tile inside the head
+    // Sub-tile whose first key row inside the head is row0 (natural order). The
+    // whole row offset goes into the per-lane offset, so the descriptor's range
+    // check (one head's bytes) covers it.
     __device__ __forceinline__ void issue(uint8_t* k_dst, uint8_t* v_dst, const uint16_t* k_head,
                                           const uint16_t* v_head, int head_bytes, int row0, int w) const {
 #pragma unroll
         for (int u = 0; u < IPW; ++u) {
             const int ins = w + WAVES * u;
-            dma16(k_head, head_bytes, k_dst + ins * 1024, voff_k[u], row0 * 256);
-            dma16(v_head, head_bytes, v_dst + ins * 1024, voff_v[u], row0 * 256);
+            dma16(k_head, head_bytes, k_dst + ins * 1024, row0 * 256 + voff_k[u], 0);
+            dma16(v_head, head_bytes, v_dst + ins * 1024, row0 * 256 + voff_v[u], 0);
+        }
+    }
+    // Same, for a head read through the frame-major map: sub-tile row r of the
+    // permuted order is natural row (r mod T) * HW + r / T; rows >= N land past
+    // the head and read as zeros.
+    __device__ __forceinline__ void issue_frame_major(uint8_t* k_dst, uint8_t* v_dst, const uint16_t* k_head,
+                                                      const uint16_t* v_head, int head_bytes, int row0, int N, int T,
+                                                      int HW, const FastDiv& div_T, int lane, int w) const {
+#pragma unroll
+        for (int u = 0; u < IPW; ++u) {
+            const int ins = w + WAVES * u;
+            const uint32_t r = (uint32_t)(row0 + 4 * ins + (lane >> 4));
+            const uint32_t s = div_T.div(r);
+            const uint32_t nat = r < (uint32_t)N ? (r - s * (uint32_t)T) * (uint32_t)HW + s : (uint32_t)N;
+            dma16(k_head, head_bytes, k_dst + ins * 1024, (int)(nat * 256u) + (voff_k[u] & 255), 0);
+            dma16(v_head, head_bytes, v_dst + ins * 1024, (int)(nat * 256u) + (voff_v[u] & 255), 0);
         }
     }
 };

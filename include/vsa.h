@@ -219,6 +219,27 @@ int vsa_block_sparse_attn_fwd(const void* q, const void* k, const void* v, void*
                               const int32_t* blk_len, const vsa_blocks* blocks, float scale,
                               void* workspace, size_t ws_bytes, void* stream);
 
+/* Block-sparse attention with the frame-major permutation folded into its
+ * loads and stores. Sparse Video-Gen page, "Approach": temporal heads work in
+ * the frame-major order (position s*T + t holds natural token t*HW + s) so that
+ * their pattern becomes dense tiles. The result equals, bit for bit,
+ *   vsa_permute(q, k, v -> FRAME_MAJOR, head_sel = head_fm),
+ *   vsa_block_sparse_attn_fwd on the permuted tensors,
+ *   vsa_permute(o -> FRAME_MAJOR, inverse, head_fm) (and LSE likewise),
+ * without the four copies: a head with head_fm[h] = 1 reads its Q, K, V rows
+ * through the map and writes O and LSE at natural positions.
+ *   q, k, v, o  [B, H, N, D] in natural order, N = g.T * g.Hh * g.W; bf16 with
+ *               D = 128 only (other dtypes or D: VSA_ERR_UNSUPPORTED), bs 64/128
+ *   lse         optional out, device fp32 [B, H, N], natural order
+ *   head_fm     host uint8 [H] (H <= 1024), 1 = frame-major head; NULL = none
+ *   blk_len, blocks, scale as for vsa_block_sparse_attn_fwd; for a frame-major
+ *               head, blocks are counted along the frame-major order
+ * No workspace; errors as for vsa_block_sparse_attn_fwd. */
+int vsa_block_sparse_attn_fwd_permuted(const void* q, const void* k, const void* v, void* o, float* lse,
+                                       int B, int H, vsa_grid g, int D, int dtype, int bs,
+                                       const uint8_t* head_fm, const int32_t* blk_len,
+                                       const vsa_blocks* blocks, float scale, void* stream);
+
 /* Validates a block list held in HOST memory: every kv_cnt in [0, max_kv], the
  * first kv_cnt entries of each row strictly ascending and inside [0, nkb).
  * Returns VSA_OK or VSA_ERR_INVALID (message names the first bad row). */

@@ -83,6 +83,26 @@ def test_attention_validation_before_any_hip_call():
     assert "exactly one" in V.vsa_last_error() or "list form" in V.vsa_last_error()
 
 
+def test_permuted_attention_validation():
+    L = V.lib()
+    fake = ctypes.c_void_p(0x1000)
+    blk = V.vsa_blocks()
+    blk.mask = 0x1000
+    hf = (ctypes.c_uint8 * 2)(1, 0)
+    call = lambda **kw: L.vsa_block_sparse_attn_fwd_permuted(
+        kw.get("q", fake), fake, fake, fake, None, 1, kw.get("H", 2), kw.get("grid", g()), kw.get("D", 128),
+        kw.get("dtype", 0), kw.get("bs", 128), ctypes.cast(hf, ctypes.c_void_p), None, ctypes.byref(blk),
+        kw.get("scale", 0.1), None)
+    assert call(q=None) == V.VSA_ERR_INVALID
+    assert call(grid=g(0)) == V.VSA_ERR_INVALID
+    assert call(D=64) == V.VSA_ERR_UNSUPPORTED            # frame-major heads: D = 128 only
+    assert "D = 128" in V.vsa_last_error()
+    assert call(dtype=1, bs=64) == V.VSA_ERR_UNSUPPORTED   # and bf16 only
+    assert call(H=2000) == V.VSA_ERR_UNSUPPORTED
+    assert call(bs=32) == V.VSA_ERR_UNSUPPORTED
+    assert call(scale=-1.0) == V.VSA_ERR_INVALID
+
+
 def test_permute_validation():
     L = V.lib()
     p = ctypes.c_void_p(0x1000)

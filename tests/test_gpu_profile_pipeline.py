@@ -95,6 +95,9 @@ def test_svg_pipeline_wan_full_shape():
     q, k, v = make_qkv(w)
     choice = [h % 2 for h in range(w.H)]
     o, sel = PL.svg_layer(dev(q), dev(k), dev(v), w.grid, w.bs, 1, 0, None, choice=choice)
+    # the fused kernel and the separate permute calls agree bit for bit
+    o_sep, _ = PL.svg_layer(dev(q), dev(k), dev(v), w.grid, w.bs, 1, 0, None, choice=choice, fused=False)
+    assert torch.equal(o, o_sep)
     rows = sample_rows(w.N, w.bs, 768, 11)
     ro, _ = OP.svg_pipeline(q, k, v, w.grid, w.bs, [choice], 1, 0, rows=rows)
     assert_close_bf16(host(o)[:, :, rows], ro, "svg pipeline")
