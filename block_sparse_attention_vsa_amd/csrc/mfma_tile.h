@@ -178,28 +178,46 @@ __device__ __forceinline__ void dma16(const void* base, int nbytes, void* lds_ds
                                              0);
 }
 
+// One dword through a buffer descriptor spanning nbytes: an offset voff at or
+// past nbytes reads 0 (the per-lane offset is range checked).
+__device__ __forceinline__ uint32_t buf_load_u32(const void* base, int nbytes, int voff, int soff) {
+    __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, nbytes,
+                                                                 0x00020000);
+    return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+}
+
 template <int WAVES>
 struct SubTileDma {
     static constexpr int IPW = kSubBytes / 1024 / WAVES;   // wave instructions per tensor per sub-tile
-    int voff_k[IPW], voff_v[IPW];   // byte offset of this lane's chunk inside the sub-tile
+    // Instruction u covers rows 4 (w + WAVES u) + (lane >> 4). Bits 0..3 of the
+    // row, which pick the K swizzle, repeat every NCLS instructions (once for 4
+    // waves); bits 0..1, which pick the V swizzle, never change with u.
+    static constexpr int NCLS = (4 * WAVES >= 16) ? 1 : 16 / (4 * WAVES);
+    int rowb;                       // byte offset of this lane's row for u = 0
+    int ck[NCLS], cv;               // swizzled chunk offsets (bytes)
     __device__ __forceinline__ SubTileDma(int lane, int w) {
+        const int p = lane & 15;
+        rowb = (4 * w + (lane >> 4)) * 256;
 #pragma unroll
-        for (int u = 0; u < IPW; ++u) {
-            const int row = 4 * (w + WAVES * u) + (lane >> 4), p = lane & 15;
-            voff_k[u] = row * 256 + ((p ^ (row & 15)) << 4);
-            voff_v[u] = row * 256 + ((p ^ (4 * (row & 3))) << 4);
+        for (int u = 0; u < NCLS; ++u) {
+            const int row = 4 * (w + WAVES * u) + (lane >> 4);
+            ck[u] = (p ^ (row & 15)) << 4;
         }
+        cv = (p ^ (4 * ((lane >> 4) & 3))) << 4;
     }
+    __device__ __forceinline__ int voff_k(int u) const { return rowb + 1024 * WAVES * u + ck[u % NCLS]; }
+    __device__ __forceinline__ int voff_v(int u) const { return rowb + 1024 * WAVES * u + cv; }
     // Sub-tile whose first key row inside the head is row0 (natural order). The
     // whole row offset goes into the per-lane offset, so the descriptor's range
     // check (one head's bytes) covers it.
     __device__ __forceinline__ void issue(uint8_t* k_dst, uint8_t* v_dst, const uint16_t* k_head,
                                           const uint16_t* v_head, int head_bytes, int row0, int w) const {
+        const int base = row0 * 256;
 #pragma unroll
         for (int u = 0; u < IPW; ++u) {
             const int ins = w + WAVES * u;
-            dma16(k_head, head_bytes, k_dst + ins * 1024, row0 * 256 + voff_k[u], 0);
-            dma16(v_head, head_bytes, v_dst + ins * 1024, row0 * 256 + voff_v[u], 0);
+            dma16(k_head, head_bytes, k_dst + ins * 1024, base + voff_k(u), 0);
+            dma16(v_head, head_bytes, v_dst + ins * 1024, base + voff_v(u), 0);
         }
     }
     // Same, for a head read through the frame-major map: sub-tile row r of the
@@ -214,8 +232,8 @@ struct SubTileDma {
             const uint32_t r = (uint32_t)(row0 + 4 * ins + (lane >> 4));
             const uint32_t s = div_T.div(r);
             const uint32_t nat = r < (uint32_t)N ? (r - s * (uint32_t)T) * (uint32_t)HW + s : (uint32_t)N;
-            dma16(k_head, head_bytes, k_dst + ins * 1024, (int)(nat * 256u) + (voff_k[u] & 255), 0);
-            dma16(v_head, head_bytes, v_dst + ins * 1024, (int)(nat * 256u) + (voff_v[u] & 255), 0);
+            dma16(k_head, head_bytes, k_dst + ins * 1024, (int)(nat * 256u) + ck[u % NCLS], 0);
+            dma16(v_head, head_bytes, v_dst + ins * 1024, (int)(nat * 256u) + cv, 0);
         }
     }
 };

@@ -5,18 +5,23 @@
 // attention; each head takes the lower-error pattern. Here the error of
 // candidate p is the sum over sampled rows and channels of (o_p - o_dense)^2.
 //
-// Four launches, no tensor is moved:
+// Launches (no tensor is moved):
 //  1. bits: for each candidate p and sampled row r, one bit per natural key n,
 //     set iff M_p[L_p(r) / bs][L_p(n) / bs] != 0, where L_p is the identity
 //     (mask stated in natural order) or the frame-major map (n -> s*T + t).
-//  2. main, one pass per output slot (dense, then each candidate; a single set
-//     of accumulators keeps 2 waves per SIMD without register spills):
-//     workgroups of 4 waves x 32 sampled rows walk a contiguous range of 64-key
-//     sub-tiles (split-K over keys, so that a few hundred rows still fill the
-//     chip), with K and V streamed into double-buffered LDS by DMA and the
-//     slot's bit words fetched one sub-tile ahead. Per sub-tile the scores S^T
-//     come from MFMA, the bits mask them, an online softmax (max, sum) runs and
-//     O^T accumulates. Each (slot, row, split) writes a partial record (m, l, O).
+//  2. main (one launch for the dense output and up to two candidates):
+//     workgroups of 4 waves cover 64 sampled rows; waves 0/1 and 2/3 take the
+//     two 32-row groups, and within a group each wave owns one half of the
+//     output channels, so three output sets fit 2 waves per SIMD. Each
+//     workgroup walks a contiguous range of 64-key sub-tiles (split-K over
+//     keys, so a few hundred rows still fill the chip), with K and V streamed
+//     into double-buffered LDS by DMA and the candidates' bit words fetched one
+//     sub-tile ahead. Per sub-tile: S^T once on MFMA, the dense online softmax
+//     (lazy running offset), and P V for the dense set. A candidate reuses the
+//     dense probabilities with its unkept keys zeroed (the same running offset
+//     serves every set), and its softmax and P V are skipped outright when
+//     none of the wave's rows keeps a key of the sub-tile. Each (slot, row,
+//     split) writes a partial record (m, l, O).
 //  3. merge: one workgroup per (b, h, sampled row) combines the partial records
 //     in split order (exact log-sum-exp rescaling), normalises every slot and
 //     sums each candidate's squared difference to the dense output.
@@ -30,10 +35,10 @@
 
 namespace vsa {
 
-constexpr int kProfRows = 128;        // sampled rows per workgroup (4 waves x 32)
+constexpr int kProfRows = 64;         // sampled rows per workgroup (2 row groups x 32)
 constexpr int kProfMaxP = 4;
 constexpr int kProfTargetWG = 512;    // 256 CUs x 2 resident workgroups
-constexpr int kProfMaxSlots = 1;      // accumulator sets per pass: one keeps 2 waves per SIMD without spills
+constexpr int kProfCandPerLaunch = 2; // candidates sharing one main launch with the dense set
 
 struct ProfPlan {
     int nsub, RT, S, TPS, words;
@@ -112,13 +117,14 @@ struct ProfArgs {
     int32_t R, N, S, TPS, nsub, words, BH;
     int64_t rec;
     float scale_log2;
-    int32_t slot_out[kProfMaxSlots];   // output slot (0 = dense, 1 + p = candidate p)
-    int32_t slot_cand[kProfMaxSlots];  // candidate whose bits apply, -1 = none
+    int32_t bits_bytes;                  // size of the bit table
+    int32_t write_dense;                 // this launch accumulates and writes slot 0 (dense)
+    int32_t cand[kProfCandPerLaunch];    // candidates handled (slot 1 + cand), -1 = none
 };
 
-template <int NC>
+template <int NCAND>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void prof_main_kernel(ProfArgs a) {
-    constexpr int D = 128, KT = kSubKeys;
+    constexpr int D = 128, KT = kSubKeys, NS = 1 + NCAND;
     constexpr float TAU = 8.f;
     // two stages as distinct LDS objects, loop unrolled by two: a DMA into one
     // stage is then provably disjoint from reads of the other
@@ -128,24 +134,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     __shared__ __attribute__((aligned(1024))) uint8_t v1[kSubBytes];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int l32 = lane & 31, half = lane >> 5;
+    const int rg = w & 1, chh = w >> 1;             // row group, channel half
     const int split = blockIdx.x, rt = blockIdx.y, bh = blockIdx.z;
     const int64_t head_off = (int64_t)bh * a.N * D;
-    const int ri = rt * kProfRows + 32 * w + l32;
+    const int ri = rt * kProfRows + 32 * rg + l32;
     const int r = ri < a.R ? a.rows[ri] : -1;
     const bool row_ok = r >= 0 && r < a.N;
-    const bool wave_active = rt * kProfRows + 32 * w < a.R;
+    const bool wave_active = rt * kProfRows + 32 * rg < a.R;
 
     bf16x8 qf[D / 16];
     load_q_frag<D>(qf, a.q + head_off + (int64_t)(row_ok ? r : 0) * D, row_ok, half);
 
-    f32x16 o[NC][D / 32];
-    float m_run[NC], l_run[NC];
+    f32x16 o[NS][2];                 // channel tiles 2 chh, 2 chh + 1 of every set
+    float l_run[NS];
+    float m_run = -INFINITY;         // running offset shared by all sets
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-        m_run[c] = -INFINITY;
+    for (int c = 0; c < NS; ++c) {
         l_run[c] = 0.f;
-#pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt) o[c][dt] = f32x16{};
+        o[c][0] = f32x16{};
+        o[c][1] = f32x16{};
     }
     const int t0 = split * a.TPS, t1 = min(t0 + a.TPS, a.nsub);
     const SubTileDma<4> dma(lane, w);
@@ -153,18 +160,30 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     auto issue = [&](int t, uint8_t* kd, uint8_t* vd) {
         dma.issue(kd, vd, a.k + head_off, a.v + head_off, head_bytes, t * KT, w);
     };
-    // candidate bit words of this lane's row, fetched one sub-tile ahead
-    auto load_bits = [&](int t, uint32_t (&wb)[NC][2]) {
+    // candidate bit words of this lane's row through a descriptor over the bit
+    // table: a 32-bit per-lane row offset (past the table, so reading 0, for a
+    // lane without a row) and the sub-tile's word as the scalar offset
+    int boff[NCAND];
 #pragma unroll
-        for (int c = 0; c < NC; ++c) {
-            const int cand = a.slot_cand[c];
+    for (int c = 0; c < NCAND; ++c)
+        boff[c] = row_ok ? (int)(((int64_t)a.cand[c] * a.R + ri) * a.words * 4) : a.bits_bytes;
+    auto load_bits = [&](int t, uint32_t (&wb)[NCAND][2]) {
+#pragma unroll
+        for (int c = 0; c < NCAND; ++c)
+#pragma unroll
+            for (int st = 0; st < 2; ++st) wb[c][st] = buf_load_u32(a.bits, a.bits_bytes, boff[c], (2 * t + st) * 4);
+    };
+    uint32_t bits_cur[NCAND][2], bits_next[NCAND][2];
+    auto pv = [&](f32x16 (&oc)[2], const bf16x8 (&pf)[2][2], const uint8_t* vt) {
+#pragma unroll
+        for (int dl = 0; dl < 2; ++dl)
 #pragma unroll
             for (int st = 0; st < 2; ++st)
-                wb[c][st] = (cand < 0) ? 0xffffffffu
-                          : (row_ok ? a.bits[((int64_t)cand * a.R + ri) * a.words + 2 * t + st] : 0u);
-        }
+#pragma unroll
+                for (int g = 0; g < 2; ++g)
+                    oc[dl] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sub_vt_operand(vt, 2 * chh + dl, st, g, lane),
+                                                                     pf[st][g], oc[dl], 0, 0, 0);
     };
-    uint32_t bits_cur[NC][2], bits_next[NC][2];
     auto compute = [&](int t, const uint8_t* kt, const uint8_t* vt) {
         if (!wave_active) return;
         const int vs = min(KT, a.N - t * KT);
@@ -177,69 +196,110 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
                 for (int x = 0; x < 16; ++x)
                     if (acc_key(st, x, half) >= vs) s[st][x] = -INFINITY;
         }
+        // dense online softmax; its offset serves every set
+        float mx = -INFINITY;
 #pragma unroll
-        for (int c = 0; c < NC; ++c) {
-            const uint32_t wbits[2] = {bits_cur[c][0], bits_cur[c][1]};
-            float mx = -INFINITY;
+        for (int st = 0; st < 2; ++st)
 #pragma unroll
-            for (int st = 0; st < 2; ++st)
+            for (int x = 0; x < 16; ++x) mx = fmaxf(mx, s[st][x]);
+        mx = pair_max(mx);
+        const float m_tile = mx * a.scale_log2;
+        const bool upd = m_tile > m_run + TAU;
+        const float m_new = upd ? m_tile : m_run;
+        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+        if (__ballot(upd)) {
+            const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
 #pragma unroll
-                for (int x = 0; x < 16; ++x)
-                    if ((wbits[st] >> (8 * (x >> 2) + 4 * half + (x & 3))) & 1u) mx = fmaxf(mx, s[st][x]);
-            mx = pair_max(mx);
-            const float m_tile = mx * a.scale_log2;
-            const bool upd = m_tile > m_run[c] + TAU;
-            const float m_new = upd ? m_tile : m_run[c];
-            const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-            if (__ballot(upd)) {
-                const float alpha = __builtin_amdgcn_exp2f(m_run[c] - m_use);
+            for (int c = 0; c < NS; ++c) {
                 l_run[c] *= alpha;
 #pragma unroll
-                for (int dt = 0; dt < D / 32; ++dt)
+                for (int dl = 0; dl < 2; ++dl)
 #pragma unroll
-                    for (int x = 0; x < 16; ++x) o[c][dt][x] *= alpha;
+                    for (int x = 0; x < 16; ++x) o[c][dl][x] *= alpha;
             }
-            m_run[c] = m_new;
-            bf16x8 pf[2][2];
-            float ps = 0.f;
+        }
+        m_run = m_new;
+        float ps[2] = {0.f, 0.f};
 #pragma unroll
-            for (int st = 0; st < 2; ++st)
+        for (int st = 0; st < 2; ++st)
+#pragma unroll
+            for (int x = 0; x < 16; ++x) {
+                s[st][x] = __builtin_amdgcn_exp2f(fmaf(s[st][x], a.scale_log2, -m_use));   // p, in place
+                ps[st] += s[st][x];
+            }
+        l_run[0] += ps[0] + ps[1];
+        // Candidates: none of the wave's rows keeps a key here -> skipped; every
+        // lane's words all-kept or all-dropped (block-aligned masks) -> the dense
+        // bf16 P with dropped lanes zeroed, after the dense P V; otherwise (keys
+        // kept one by one) P from the fp32 values first, so that those die
+        // before the dense bf16 copy exists.
+        bool any[NCAND], whole[NCAND];
+#pragma unroll
+        for (int c = 0; c < NCAND; ++c) {
+            const uint32_t b0 = bits_cur[c][0], b1 = bits_cur[c][1];
+            any[c] = __ballot((b0 | b1) != 0u) != 0;
+            whole[c] = __ballot((b0 + 1u > 1u) || (b1 + 1u > 1u)) == 0;
+        }
+#pragma unroll
+        for (int c = 0; c < NCAND; ++c) {
+            if (!any[c] || whole[c]) continue;
+            bf16x8 pc[2][2];
+            float lc = 0.f;
+#pragma unroll
+            for (int st = 0; st < 2; ++st) {
+                const uint32_t wb = bits_cur[c][st];
 #pragma unroll
                 for (int x = 0; x < 16; ++x) {
-                    const bool keep = (wbits[st] >> (8 * (x >> 2) + 4 * half + (x & 3))) & 1u;
-                    const float p = keep ? __builtin_amdgcn_exp2f(fmaf(s[st][x], a.scale_log2, -m_use)) : 0.f;
-                    ps += p;
-                    pf[st][x >> 3][x & 7] = (__bf16)p;
+                    const bool keep = (wb >> (8 * (x >> 2) + 4 * half + (x & 3))) & 1u;
+                    const float pk = keep ? s[st][x] : 0.f;
+                    lc += pk;
+                    pc[st][x >> 3][x & 7] = (__bf16)pk;
                 }
-            l_run[c] += ps;
+            }
+            l_run[1 + c] += lc;
+            pv(o[1 + c], pc, vt);
+        }
+        bf16x8 pf[2][2];
 #pragma unroll
-            for (int dt = 0; dt < D / 32; ++dt)
+        for (int st = 0; st < 2; ++st)
 #pragma unroll
-                for (int st = 0; st < 2; ++st)
+            for (int x = 0; x < 16; ++x) pf[st][x >> 3][x & 7] = (__bf16)s[st][x];
+        if (a.write_dense) pv(o[0], pf, vt);
 #pragma unroll
-                    for (int g = 0; g < 2; ++g)
-                        o[c][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sub_vt_operand(vt, dt, st, g, lane),
-                                                                           pf[st][g], o[c][dt], 0, 0, 0);
+        for (int c = 0; c < NCAND; ++c) {
+            if (!any[c] || !whole[c]) continue;
+            const uint32_t b0 = bits_cur[c][0], b1 = bits_cur[c][1];
+            const bf16x8 zero = bf16x8{};
+            bf16x8 pc[2][2];
+#pragma unroll
+            for (int g = 0; g < 2; ++g) {
+                pc[0][g] = b0 ? pf[0][g] : zero;
+                pc[1][g] = b1 ? pf[1][g] : zero;
+            }
+            l_run[1 + c] += (b0 ? ps[0] : 0.f) + (b1 ? ps[1] : 0.f);
+            pv(o[1 + c], pc, vt);
         }
     };
     auto rotate = [&]() {
 #pragma unroll
-        for (int c = 0; c < NC; ++c) {
+        for (int c = 0; c < NCAND; ++c) {
             bits_cur[c][0] = bits_next[c][0];
             bits_cur[c][1] = bits_next[c][1];
         }
     };
+    // the bit words are loaded before the DMA, so waiting for them never waits
+    // for the tiles behind them
     if (t0 < t1) {
-        issue(t0, k0, v0);
         load_bits(t0, bits_next);
+        issue(t0, k0, v0);
     }
     for (int t = t0; t < t1; t += 2) {
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         rotate();
         if (t + 1 < t1) {
-            issue(t + 1, k1, v1);
             load_bits(t + 1, bits_next);
+            issue(t + 1, k1, v1);
         }
         compute(t, k0, v0);
         if (t + 1 < t1) {
@@ -247,28 +307,30 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
             __syncthreads();
             rotate();
             if (t + 2 < t1) {
-                issue(t + 2, k0, v0);
                 load_bits(t + 2, bits_next);
+                issue(t + 2, k0, v0);
             }
             compute(t + 1, k1, v1);
         }
     }
     if (!wave_active) return;
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
+    for (int c = 0; c < NS; ++c) {
+        if (c == 0 && !a.write_dense) continue;
         const float l_tot = pair_sum(l_run[c]);
         if (ri >= a.R) continue;
-        float* rec = a.part + ((((int64_t)a.slot_out[c] * a.BH + bh) * a.R + ri) * a.S + split) * a.rec;
-        if (half == 0) {
-            rec[0] = m_run[c];
+        const int slot = c == 0 ? 0 : 1 + a.cand[c - 1];
+        float* rec = a.part + ((((int64_t)slot * a.BH + bh) * a.R + ri) * a.S + split) * a.rec;
+        if (chh == 0 && half == 0) {
+            rec[0] = m_run;
             rec[1] = l_tot;
         }
 #pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt)
+        for (int dl = 0; dl < 2; ++dl)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                f32x4 v4 = {o[c][dt][4 * j], o[c][dt][4 * j + 1], o[c][dt][4 * j + 2], o[c][dt][4 * j + 3]};
-                *reinterpret_cast<f32x4*>(rec + 4 + 32 * dt + 8 * j + 4 * half) = v4;
+                f32x4 v4 = {o[c][dl][4 * j], o[c][dl][4 * j + 1], o[c][dl][4 * j + 2], o[c][dl][4 * j + 3]};
+                *reinterpret_cast<f32x4*>(rec + 4 + 32 * (2 * chh + dl) + 8 * j + 4 * half) = v4;
             }
     }
 }
@@ -374,6 +436,8 @@ extern "C" int vsa_profile_heads(const void* q, const void* k, const void* v, in
     if (N >= (1ll << 31) || R > N) return fail(VSA_ERR_INVALID, "vsa_profile_heads: bad N or R");
     if ((int64_t)B * H > 65535 || R > 65535) return fail(VSA_ERR_INVALID, "vsa_profile_heads: B*H or R too large");
     const ProfPlan pl = prof_plan(B, H, N, D, R, P);
+    if ((int64_t)P * R * pl.words * 4 >= (1ll << 31))
+        return fail(VSA_ERR_INVALID, "vsa_profile_heads: candidate bit table exceeds 2 GiB (R or N too large)");
     if (!workspace || ws_bytes < pl.total)
         return fail(VSA_ERR_WORKSPACE, "vsa_profile_heads: workspace of %zu bytes needed (got %zu)", pl.total, ws_bytes);
     hipStream_t s = as_stream(stream);
@@ -396,18 +460,16 @@ extern "C" int vsa_profile_heads(const void* q, const void* k, const void* v, in
     pa.rows = rows; pa.bits = ba.bits; pa.part = reinterpret_cast<float*>(ws + pl.off_part);
     pa.R = R; pa.N = (int32_t)N; pa.S = pl.S; pa.TPS = pl.TPS; pa.nsub = pl.nsub; pa.words = pl.words;
     pa.BH = B * H; pa.rec = pl.rec;
+    pa.bits_bytes = (int32_t)((size_t)P * R * pl.words * 4);
     pa.scale_log2 = (float)((double)scale * 1.4426950408889634);
     dim3 grid(pl.S, pl.RT, B * H);
-    // output slots 0 (dense) .. P, one accumulator set per pass
-    for (int first = 0; first <= P; first += kProfMaxSlots) {
-        const int nc = std::min(kProfMaxSlots, P + 1 - first);
-        for (int c = 0; c < kProfMaxSlots; ++c) {
-            const int slot = first + std::min(c, nc - 1);
-            pa.slot_out[c] = slot;
-            pa.slot_cand[c] = slot - 1;
-        }
-        (void)nc;
-        hipLaunchKernelGGL(prof_main_kernel<1>, grid, dim3(256), 0, s, pa);
+    // the dense set and up to two candidates per launch (S recomputed per launch)
+    for (int first = 0; first < P; first += kProfCandPerLaunch) {
+        const int nc = std::min(kProfCandPerLaunch, P - first);
+        pa.write_dense = first == 0;
+        for (int c = 0; c < kProfCandPerLaunch; ++c) pa.cand[c] = c < nc ? first + c : -1;
+        if (nc == 2) hipLaunchKernelGGL(prof_main_kernel<2>, grid, dim3(256), 0, s, pa);
+        else hipLaunchKernelGGL(prof_main_kernel<1>, grid, dim3(256), 0, s, pa);
         st = launch_status("vsa_profile_heads (main)");
         if (st) return st;
     }
