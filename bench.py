@@ -245,32 +245,32 @@ def main():
         e1 = T.ev()
         _, ch = V.vsa_profile_heads(q, k, v, grid, bs, rows, cand, [0, 1], workspace=ws)
         e2 = T.ev()
-        sel = ch[0].cpu().tolist()
+        # a6 + a3 + a7 + a8 in one launch: the kernel reads each head's choice,
+        # compacts the chosen mask row and applies the frame-major order of
+        # temporal heads in its loads and stores; no host round trip in the step
+        o = V.vsa_block_sparse_attn_fwd_chosen(q, k, v, grid, bs, cand, [0, 1], ch)
         e3 = T.ev()
-        idx, cnt = V.vsa_mask_to_list(cand, head_mask_idx=sel, B=B)
-        e4 = T.ev()
-        # a3 + a7 + a8: the frame-major permutation of the temporal heads is done
-        # by the attention kernel's loads and stores
-        o = V.vsa_block_sparse_attn_fwd_permuted(q, k, v, grid, bs, head_fm=sel, kv_idx=idx, kv_cnt=cnt)
-        e5 = T.ev()
         if timed:
-            for key, a, b in (("a1_pattern_masks", e0, e1), ("a2_profile", e1, e2), ("choice_sync", e2, e3),
-                              ("a6_mask_to_list", e3, e4), ("a3_a7_a8_attention_fused_permute", e4, e5)):
+            for key, a, b in (("a1_pattern_masks", e0, e1), ("a2_profile", e1, e2),
+                              ("a3_a6_a7_a8_attention", e2, e3)):
                 T.add(key, a, b)
-        return o, sel, idx, cnt
+        return o, ch, cand
 
     for _ in range(args.warmup):
         step(False)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        o, sel, idx, cnt = step(True)
+        o, ch, cand = step(True)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = wall * 1e3 / args.steps
 
+    # kept blocks of the last step's choice (outside the timed region)
+    sel = [int(c) for c in ch[0].cpu().tolist()]
+    idx, cnt = V.vsa_mask_to_list(cand, head_mask_idx=sel, B=B)
     flops = kept_flops_from_lists(idx, cnt, N, bs, D)
-    attn_ms = T.mean_ms("a3_a7_a8_attention_fused_permute")
+    attn_ms = T.mean_ms("a3_a6_a7_a8_attention")
     attn_tflops = flops / (attn_ms * 1e-3) / 1e12
     comp = {key: round(T.mean_ms(key), 4) for key in T.acc}
 
@@ -323,10 +323,11 @@ def main():
         extra = extra_layers(torch, V, PL, T)
 
     digest = source_digest("attn_fwd.hip", "mfma_tile.h", "vsa_internal.h")
-    traffic = stored_traffic("attn_fwd_bf16_d128_kernel<128>/wan480_svg", digest)
+    kname = f"attn_fwd_bf16_d128_kernel<128, {'true' if n_moved else 'false'}>"
+    traffic = stored_traffic(f"{kname}/wan480_svg", digest)
     roofline = {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
-                "kernel": "attn_fwd_bf16_d128_kernel<128>", "per_launch_flops": flops,
+                "kernel": kname, "per_launch_flops": flops,
                 "avg_launch_ms": round(attn_ms, 4)}
 
     cpu = None
@@ -347,7 +348,7 @@ def main():
         "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "wan2.1-1.3B 480p layer, Sparse VideoGen step (profile 1% rows, spatial w=1 / "
-                               "temporal w=0 per head, frame-major order of temporal heads folded into the attention kernel)",
+                               "temporal w=0 per head; the attention kernel reads the choice, the chosen mask and the frame-major order of temporal heads itself)",
                    "B": B, "H": H, "N": N, "D": D, "grid": list(grid), "block": bs,
                    "heads_temporal": int(n_moved), "kept_block_density": round(float(cnt.sum().item()) / (B * H * w.nb * w.nb), 4)},
         "pct_mfma_peak_step": round(100 * value / PEAK_BF16_TFLOPS, 2),

@@ -59,6 +59,8 @@ _SIGNATURES = {
                                        ctypes.POINTER(vsa_blocks), _F, _P, _SZ, _P]),
     "vsa_block_sparse_attn_fwd_permuted": (_I, [_P, _P, _P, _P, _P, _I, _I, vsa_grid, _I, _I, _I, _P, _P,
                                                 ctypes.POINTER(vsa_blocks), _F, _P]),
+    "vsa_block_sparse_attn_fwd_chosen": (_I, [_P, _P, _P, _P, _P, _I, _I, vsa_grid, _I, _I, _I, _P, _P, _I, _P,
+                                              _P, _F, _P]),
     "vsa_check_block_list_host": (_I, [_P, _P, _I64, _I, _I]),
 }
 
@@ -370,6 +372,43 @@ def vsa_block_sparse_attn_fwd_permuted(q, k, v, grid, bs: int, head_fm=None, mas
                                                     _grid(grid), D, _dtype_code(q), bs, hf, _ptr(blk_len),
                                                     ctypes.byref(blocks), scale, _stream(q.device)),
            "vsa_block_sparse_attn_fwd_permuted")
+    return (out, lse) if return_lse else out
+
+
+def vsa_block_sparse_attn_fwd_chosen(q, k, v, grid, bs: int, cand_masks, cand_layout, choice, blk_len=None,
+                                     scale=None, return_lse=False, out=None, lse=None):
+    """Attention with head (b, h) using candidate mask cand_masks[choice[b, h]]
+    in layout cand_layout[choice[b, h]]; `choice` is a device int32 [B, H]
+    tensor (e.g. vsa_profile_heads' output), read by the kernel."""
+    torch = _torch()
+    _need(q, "q", ndim=4)
+    _need(k, "k", q.dtype, 4)
+    _need(v, "v", q.dtype, 4)
+    B, H, N, D = q.shape
+    if k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must have the same shape")
+    if N != int(np.prod(grid)):
+        raise ValueError("N must equal T*Hh*W")
+    _need(cand_masks, "cand_masks", torch.uint8, 3)
+    _need(choice, "choice", torch.int32)
+    if choice.numel() != B * H:
+        raise ValueError("choice needs B*H entries")
+    P = cand_masks.shape[0]
+    if len(cand_layout) != P:
+        raise ValueError("cand_layout needs one entry per candidate")
+    lay = (ctypes.c_int32 * P)(*[int(x) for x in cand_layout])
+    scale = default_scale(D) if scale is None else scale
+    if out is None:
+        out = torch.empty_like(q)
+    if return_lse and lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    if blk_len is not None:
+        _need(blk_len, "blk_len", torch.int32, 1)
+    _check(lib().vsa_block_sparse_attn_fwd_chosen(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, _grid(grid),
+                                                  D, _dtype_code(q), bs, _ptr(cand_masks),
+                                                  ctypes.cast(lay, ctypes.c_void_p), P, _ptr(choice), _ptr(blk_len),
+                                                  scale, _stream(q.device)),
+           "vsa_block_sparse_attn_fwd_chosen")
     return (out, lse) if return_lse else out
 
 

@@ -49,6 +49,12 @@ struct AttnArgs {
     int32_t T, HW;
     FastDiv div_T;
     uint32_t fm_bits[32];  // bit h set: head h is in frame-major order; all zero otherwise
+    // per-(b, h) candidate choice read on the device (D = 128 bf16 kernel only):
+    // the mask rows come from mask[choice[b, h]] ([n_cand, nb, nb]) and the
+    // layout from cand_fm[choice[b, h]]; fm_bits is unused then
+    const int32_t* head_choice;
+    int32_t n_cand;
+    int32_t cand_fm[4];
 };
 
 // Natural row of permuted row r (r < N) for a frame-major head.
@@ -275,15 +281,23 @@ __global__ __launch_bounds__(BS * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
     // frame-major head (uniform over the workgroup); launches without any such
     // head use the GATHER = false instance, which carries no code for it
     bool fm = false;
-    if constexpr (GATHER) {
+    const uint8_t* mask_row = a.mask ? a.mask + (int64_t)item * nkb : nullptr;
+    if (a.head_choice) {
+        const int c = ld_const(a.head_choice, bh);
+        const bool ok = (unsigned)c < (unsigned)a.n_cand;     // otherwise: nothing kept
+        mask_row = ok ? a.mask + ((int64_t)c * nqb + qb) * nkb : nullptr;
+        if constexpr (GATHER) fm = ok && a.cand_fm[ok ? c : 0] != 0;
+    } else if constexpr (GATHER) {
         const int h = bh % a.H;
         fm = (a.fm_bits[h >> 5] >> (h & 31)) & 1u;
     }
 
     int cnt;
     const int32_t* list_g = nullptr;
-    if (a.mask) {
-        cnt = compact_mask_row<THREADS>(a.mask + (int64_t)item * nkb, nkb, list_lds, wave_cnt);
+    if (a.head_choice && !mask_row) {
+        cnt = 0;
+    } else if (a.mask) {
+        cnt = compact_mask_row<THREADS>(mask_row, nkb, list_lds, wave_cnt);
     } else {
         cnt = min(ld_const(a.kv_cnt, item), a.max_kv);
         list_g = a.kv_idx + (int64_t)item * a.max_kv;
@@ -576,6 +590,8 @@ void launch_attn(const AttnArgs& a, int D, int dtype, int bs, hipStream_t s) {
     if (dtype == VSA_BF16) {
         bool gather = false;
         for (int i = 0; i < 32; ++i) gather |= a.fm_bits[i] != 0;
+        if (a.head_choice)
+            for (int c = 0; c < a.n_cand; ++c) gather |= a.cand_fm[c] != 0;
         if (D == 128 && bs == 128) {
             if (gather) hipLaunchKernelGGL((attn_fwd_bf16_d128_kernel<128, true>), grid, dim3(256), 0, s, a);
             else hipLaunchKernelGGL((attn_fwd_bf16_d128_kernel<128, false>), grid, dim3(256), 0, s, a);
@@ -626,6 +642,35 @@ extern "C" int vsa_block_sparse_attn_fwd_permuted(const void* q, const void* k, 
     if (head_fm)
         for (int h = 0; h < H; ++h)
             if (head_fm[h]) a.fm_bits[h >> 5] |= 1u << (h & 31);
+    launch_attn(a, D, dtype, bs, as_stream(stream));
+    return launch_status(fn);
+}
+
+extern "C" int vsa_block_sparse_attn_fwd_chosen(const void* q, const void* k, const void* v, void* o, float* lse,
+                                                int B, int H, vsa_grid g, int D, int dtype, int bs,
+                                                const uint8_t* cand_masks, const int32_t* cand_layout, int P,
+                                                const int32_t* choice, const int32_t* blk_len, float scale,
+                                                void* stream) {
+    const char* fn = "vsa_block_sparse_attn_fwd_chosen";
+    if (!cand_masks || !cand_layout || !choice) return fail(VSA_ERR_INVALID, "%s: null pointer", fn);
+    if (P < 1 || P > 4) return fail(VSA_ERR_INVALID, "%s: P must be in [1, 4]", fn);
+    for (int c = 0; c < P; ++c)
+        if (cand_layout[c] != 0 && cand_layout[c] != 1)
+            return fail(VSA_ERR_INVALID, "%s: cand_layout[%d] must be 0 or 1", fn, c);
+    if (g.T <= 0 || g.Hh <= 0 || g.W <= 0) return fail(VSA_ERR_INVALID, "%s: grid extents must be positive", fn);
+    const int64_t N64 = (int64_t)g.T * g.Hh * g.W;
+    if (N64 >= (1ll << 31)) return fail(VSA_ERR_INVALID, "%s: grid too large", fn);
+    vsa_blocks blocks{cand_masks, nullptr, nullptr, 0};
+    AttnArgs a;
+    const int st = prepare_attn(fn, a, q, k, v, o, lse, B, H, (int)N64, D, dtype, bs, blk_len, &blocks, scale);
+    if (st != VSA_OK) return st;
+    if (dtype != VSA_BF16 || D != 128) return fail(VSA_ERR_UNSUPPORTED, "%s: needs bf16 with D = 128", fn);
+    a.T = g.T;
+    a.HW = g.Hh * g.W;
+    a.div_T = FastDiv((uint32_t)g.T);
+    a.head_choice = choice;
+    a.n_cand = P;
+    for (int c = 0; c < P; ++c) a.cand_fm[c] = cand_layout[c];
     launch_attn(a, D, dtype, bs, as_stream(stream));
     return launch_status(fn);
 }

@@ -5,8 +5,8 @@ their outputs; every step runs in a HIP kernel.
 
 * svg_layer: Sparse Video-Gen page, "Approach": pattern masks, per-head choice
   from sampled rows, frame-major permutation of temporal heads, block-sparse
-  attention, inverse permutation (by default the two permutations are folded
-  into the attention kernel's loads and stores).
+  attention, inverse permutation (by default the choice is read on the device
+  and the two permutations are folded into the attention kernel).
 * cube_layer: USV page, Figure 2 caption (3D cubes, top-k cube selection) with
   the top-p budget of the Sparse VideoGen2 page, Abstract.
 * long_layer: machinebrief LVSA article (block-sparse attention at a long
@@ -17,7 +17,7 @@ from __future__ import annotations
 import math
 
 from . import (VSA_PATTERN_SPATIAL, VSA_PATTERN_TEMPORAL, VSA_PERM_CUBE4, VSA_PERM_FRAME_MAJOR,
-               vsa_block_scores, vsa_block_sparse_attn_fwd, vsa_block_sparse_attn_fwd_permuted,
+               vsa_block_scores, vsa_block_sparse_attn_fwd, vsa_block_sparse_attn_fwd_chosen,
                vsa_cube_block_len, vsa_cube_dims, vsa_mask_to_list,
                vsa_pattern_mask, vsa_permute, vsa_profile_heads, vsa_select_topk)
 
@@ -37,10 +37,15 @@ def svg_masks(grid, bs, w_spatial, w_temporal, device="cuda"):
 def svg_layer(q, k, v, grid, bs, w_spatial, w_temporal, rows, scale=None, choice=None, cand=None, workspace=None,
               stats=None, fused=True):
     """Returns (o, choice_host). `choice` [H] (host) skips the profiler; `rows`
-    (device int32) are the sampled query rows otherwise. With `fused` the
-    frame-major permutation of the temporal heads happens inside the attention
-    kernel's loads and stores; otherwise as separate permute calls (same
-    result, bit for bit)."""
+    (device int32) are the sampled query rows otherwise.
+
+    fused (default): the attention kernel reads each head's choice on the device,
+    compacts the chosen candidate's mask rows itself and applies the frame-major
+    order of temporal heads in its loads and stores; the host copy of the choice
+    is taken after the attention launch. fused=False: the same result, bit for
+    bit, through host choice -> mask -> list -> permute -> attention -> inverse
+    permute."""
+    import torch
     B, H = q.shape[:2]
     if B != 1:
         raise ValueError("svg_layer permutes heads by a per-head choice; call it per batch entry")
@@ -48,17 +53,18 @@ def svg_layer(q, k, v, grid, bs, w_spatial, w_temporal, rows, scale=None, choice
         cand = svg_masks(grid, bs, w_spatial, w_temporal, q.device)
     if choice is None:
         _, ch = vsa_profile_heads(q, k, v, grid, bs, rows, cand, [0, 1], scale=scale, workspace=workspace)
-        choice = ch[0].cpu().tolist()                       # host decision: which heads move
-    sel = [int(c) for c in choice]
-    idx, cnt = vsa_mask_to_list(cand, head_mask_idx=sel, B=B)
+    else:
+        ch = torch.tensor([[int(c) for c in choice]], dtype=torch.int32, device=q.device)
     if fused:
-        o = vsa_block_sparse_attn_fwd_permuted(q, k, v, grid, bs, head_fm=sel, kv_idx=idx, kv_cnt=cnt, scale=scale)
+        o = vsa_block_sparse_attn_fwd_chosen(q, k, v, grid, bs, cand, [0, 1], ch, scale=scale)
         if stats is not None:
-            stats.update(kv_idx=idx, kv_cnt=cnt, cand=cand)
-        return o, sel
+            stats.update(cand=cand, choice=ch)
+        return o, [int(c) for c in ch[0].cpu().tolist()]
+    sel = [int(c) for c in ch[0].cpu().tolist()]           # host decision: which heads move
     qm = vsa_permute(q, grid, VSA_PERM_FRAME_MAJOR, False, sel)
     km = vsa_permute(k, grid, VSA_PERM_FRAME_MAJOR, False, sel)
     vm = vsa_permute(v, grid, VSA_PERM_FRAME_MAJOR, False, sel)
+    idx, cnt = vsa_mask_to_list(cand, head_mask_idx=sel, B=B)
     om = vsa_block_sparse_attn_fwd(qm, km, vm, bs, kv_idx=idx, kv_cnt=cnt, scale=scale)
     o = vsa_permute(om, grid, VSA_PERM_FRAME_MAJOR, True, sel)
     if stats is not None:

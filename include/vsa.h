@@ -240,6 +240,28 @@ int vsa_block_sparse_attn_fwd_permuted(const void* q, const void* k, const void*
                                        const uint8_t* head_fm, const int32_t* blk_len,
                                        const vsa_blocks* blocks, float scale, void* stream);
 
+/* Block-sparse attention in which every head uses the candidate pattern chosen
+ * for it on the device (Sparse Video-Gen page, "Approach": each head takes the
+ * pattern whose output on sampled rows is closest to dense attention). The
+ * result equals, bit for bit, vsa_block_sparse_attn_fwd_permuted with head
+ * (b, h) using block mask cand_masks[choice[b, h]] and head_fm =
+ * cand_layout[choice[b, h]]; the choice is read by the kernel, so no host round
+ * trip and no mask -> list step sit between the profiler and the attention.
+ *   q, k, v, o   [B, H, N, D] natural order, N = g.T * g.Hh * g.W; bf16, D = 128,
+ *                bs 64 or 128 (otherwise VSA_ERR_UNSUPPORTED); nb <= 4096
+ *   lse          optional out, device fp32 [B, H, N], natural order
+ *   cand_masks   device uint8 [P, nb, nb]; a frame-major candidate's mask counts
+ *                blocks along the frame-major order
+ *   cand_layout  host int32 [P]: 0 natural, 1 frame-major; P in [1, 4]
+ *   choice       device int32 [B, H] (e.g. from vsa_profile_heads); an entry
+ *                outside [0, P) keeps nothing: O = 0, LSE = -inf for that head
+ *   blk_len, scale as for vsa_block_sparse_attn_fwd. No workspace. */
+int vsa_block_sparse_attn_fwd_chosen(const void* q, const void* k, const void* v, void* o, float* lse,
+                                     int B, int H, vsa_grid g, int D, int dtype, int bs,
+                                     const uint8_t* cand_masks, const int32_t* cand_layout, int P,
+                                     const int32_t* choice, const int32_t* blk_len, float scale,
+                                     void* stream);
+
 /* Validates a block list held in HOST memory: every kv_cnt in [0, max_kv], the
  * first kv_cnt entries of each row strictly ascending and inside [0, nkb).
  * Returns VSA_OK or VSA_ERR_INVALID (message names the first bad row). */

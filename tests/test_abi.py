@@ -103,6 +103,24 @@ def test_permuted_attention_validation():
     assert call(scale=-1.0) == V.VSA_ERR_INVALID
 
 
+def test_chosen_attention_validation():
+    L = V.lib()
+    fake = ctypes.c_void_p(0x1000)
+    lay = (ctypes.c_int32 * 2)(0, 1)
+    bad = (ctypes.c_int32 * 2)(0, 3)
+    call = lambda **kw: L.vsa_block_sparse_attn_fwd_chosen(
+        fake, fake, fake, fake, None, 1, 2, kw.get("grid", g()), kw.get("D", 128), 0, 128,
+        kw.get("cand", fake), ctypes.cast(kw.get("lay", lay), ctypes.c_void_p), kw.get("P", 2),
+        kw.get("choice", fake), None, 0.1, None)
+    assert call(cand=None) == V.VSA_ERR_INVALID
+    assert call(choice=None) == V.VSA_ERR_INVALID
+    assert call(P=0) == V.VSA_ERR_INVALID
+    assert call(P=5) == V.VSA_ERR_INVALID
+    assert call(lay=bad) == V.VSA_ERR_INVALID
+    assert call(grid=g(0)) == V.VSA_ERR_INVALID
+    assert call(D=64) == V.VSA_ERR_UNSUPPORTED
+
+
 def test_permute_validation():
     L = V.lib()
     p = ctypes.c_void_p(0x1000)

@@ -112,3 +112,43 @@ def test_fused_wan_full_shape_mixed_heads():
     mask = cand[head_fm][None]
     ro, _ = oracle_mixed(host(qd), host(kd), host(vd), w.grid, w.bs, mask, head_fm, rows=rows)
     assert_close_bf16(host(o_f)[:, :, rows], ro, "fused wan")
+
+
+@pytest.mark.parametrize("grid,bs", [((5, 6, 10), 64), ((7, 9, 11), 128)])
+def test_chosen_matches_permuted_per_head_masks(grid, bs):
+    """Device-side choice: B = 2, per-(b, h) choices over two candidates (natural
+    and frame-major), one out-of-range entry (that head keeps nothing)."""
+    B, H = 2, 3
+    N = int(np.prod(grid))
+    nb = -(-N // bs)
+    announce(f"chosen attn grid={grid} bs={bs}")
+    rng = np.random.default_rng(N * 7 + bs)
+    qd, kd, vd = (dev(rng.standard_normal((B, H, N, 128)).astype(np.float32)) for _ in range(3))
+    cand = (rng.random((2, nb, nb)) < 0.4).astype(np.uint8)
+    layout = [0, 1]
+    choice = np.array([[0, 1, 1], [1, 7, 0]], np.int32)
+    o_c, l_c = V.vsa_block_sparse_attn_fwd_chosen(qd, kd, vd, grid, bs, dev_u8(cand), layout, dev_i32(choice),
+                                                  return_lse=True)
+    for b in range(B):
+        ok = (choice[b] >= 0) & (choice[b] < 2)
+        masks = np.stack([cand[c] if o else np.zeros((nb, nb), np.uint8) for c, o in zip(choice[b], ok)])[None]
+        head_fm = [layout[c] if o else 0 for c, o in zip(choice[b], ok)]
+        o_p, l_p = V.vsa_block_sparse_attn_fwd_permuted(qd[b:b + 1].contiguous(), kd[b:b + 1].contiguous(),
+                                                        vd[b:b + 1].contiguous(), grid, bs, head_fm=head_fm,
+                                                        mask=dev_u8(masks), return_lse=True)
+        assert torch.equal(o_c[b:b + 1], o_p), f"batch {b}: output differs"
+        assert torch.equal(l_c[b:b + 1], l_p), f"batch {b}: LSE differs"
+    assert (host(o_c)[1, 1] == 0).all() and np.isneginf(host(l_c)[1, 1]).all()
+
+
+def test_chosen_wan_full_shape_matches_list_path():
+    w = WAN480
+    announce("chosen attn wan full")
+    q, k, v = make_qkv(w)
+    qd, kd, vd = dev(q), dev(k), dev(v)
+    sel = [(h * 5) % 3 % 2 for h in range(w.H)]
+    cand = dev_u8(np.stack([OM.pattern_mask(w.grid, w.bs, "spatial", 1), OM.pattern_mask(w.grid, w.bs, "temporal", 0)]))
+    o_c = V.vsa_block_sparse_attn_fwd_chosen(qd, kd, vd, w.grid, w.bs, cand, [0, 1], dev_i32(np.array([sel])))
+    idx, cnt = V.vsa_mask_to_list(cand, head_mask_idx=sel, B=1)
+    o_l = V.vsa_block_sparse_attn_fwd_permuted(qd, kd, vd, w.grid, w.bs, head_fm=sel, kv_idx=idx, kv_cnt=cnt)
+    assert torch.equal(o_c, o_l)
