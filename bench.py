@@ -323,7 +323,9 @@ def main():
         extra = extra_layers(torch, V, PL, T)
 
     digest = source_digest("attn_fwd.hip", "mfma_tile.h", "vsa_internal.h")
-    kname = f"attn_fwd_bf16_d128_kernel<128, {'true' if n_moved else 'false'}>"
+    # the chosen-candidate launch carries the frame-major loop whenever a
+    # candidate is frame-major (decided on the device per head)
+    kname = "attn_fwd_bf16_d128_kernel<128, true>"
     traffic = stored_traffic(f"{kname}/wan480_svg", digest)
     roofline = {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic,

@@ -311,13 +311,18 @@ __global__ __launch_bounds__(BS * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
     };
     const SubTileDma<WAVES> dma(lane, w);
     const int head_bytes = a.N * D * 2;
-    auto issue = [&](int i, uint8_t* kd, uint8_t* vd) {
+    // natural rows / rows through the frame-major map; the main loop below is
+    // instantiated once per form, so a natural head runs no gather code
+    auto issue_nat = [&](int i, uint8_t* kd, uint8_t* vd) {
         int kb;
-        const int vs = sub_valid(i, kb);
-        if (vs == 0) return;
-        const int row0 = kb * BS + (i % SUB) * KT;
-        if (fm) dma.issue_frame_major(kd, vd, a.k + head_off, a.v + head_off, head_bytes, row0, a.N, a.T, a.HW, a.div_T, lane, w);
-        else dma.issue(kd, vd, a.k + head_off, a.v + head_off, head_bytes, row0, w);
+        if (sub_valid(i, kb) == 0) return;
+        dma.issue(kd, vd, a.k + head_off, a.v + head_off, head_bytes, kb * BS + (i % SUB) * KT, w);
+    };
+    auto issue_fm = [&](int i, uint8_t* kd, uint8_t* vd) {
+        int kb;
+        if (sub_valid(i, kb) == 0) return;
+        dma.issue_frame_major(kd, vd, a.k + head_off, a.v + head_off, head_bytes, kb * BS + (i % SUB) * KT, a.N, a.T,
+                              a.HW, a.div_T, lane, w);
     };
 
     const int q_local = 32 * w + l32;
@@ -333,7 +338,7 @@ __global__ __launch_bounds__(BS * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
     for (int dt = 0; dt < D / 32; ++dt) o_acc[dt] = f32x16{};
     float m_run = -INFINITY, l_run = 0.f;
 
-    auto compute = [&](int i, const uint8_t* kt, const uint8_t* vt) {
+    auto compute = [&](int i, const uint8_t* kt, const uint8_t* vt) __attribute__((always_inline)) {
         int kb;
         const int vs = sub_valid(i, kb);
         if (!wave_active || vs == 0) return;
@@ -392,29 +397,33 @@ __global__ __launch_bounds__(BS * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
     };
 
     const int n_sub = cnt * SUB;
-    if (n_sub > 0) issue(0, k0, v0);
-    if constexpr (TWO_STAGES) {
-        for (int i = 0; i < n_sub; i += 2) {
-            __builtin_amdgcn_s_waitcnt(0);          // this thread's copies of sub-tile i have landed
-            __syncthreads();                        // ... and everyone's; stage 1 is free again
-            if (i + 1 < n_sub) issue(i + 1, k1, v1);
-            compute(i, k0, v0);
-            if (i + 1 < n_sub) {
+    auto main_loop = [&](auto issue) __attribute__((always_inline)) {
+        if (n_sub > 0) issue(0, k0, v0);
+        if constexpr (TWO_STAGES) {
+            for (int i = 0; i < n_sub; i += 2) {
+                __builtin_amdgcn_s_waitcnt(0);      // this thread's copies of sub-tile i have landed
+                __syncthreads();                    // ... and everyone's; stage 1 is free again
+                if (i + 1 < n_sub) issue(i + 1, k1, v1);
+                compute(i, k0, v0);
+                if (i + 1 < n_sub) {
+                    __builtin_amdgcn_s_waitcnt(0);
+                    __syncthreads();
+                    if (i + 2 < n_sub) issue(i + 2, k0, v0);
+                    compute(i + 1, k1, v1);
+                }
+            }
+        } else {
+            for (int i = 0; i < n_sub; ++i) {
                 __builtin_amdgcn_s_waitcnt(0);
                 __syncthreads();
-                if (i + 2 < n_sub) issue(i + 2, k0, v0);
-                compute(i + 1, k1, v1);
+                compute(i, k0, v0);
+                __syncthreads();                    // stage free before the next copy
+                if (i + 1 < n_sub) issue(i + 1, k0, v0);
             }
         }
-    } else {
-        for (int i = 0; i < n_sub; ++i) {
-            __builtin_amdgcn_s_waitcnt(0);
-            __syncthreads();
-            compute(i, k0, v0);
-            __syncthreads();                        // stage free before the next copy
-            if (i + 1 < n_sub) issue(i + 1, k0, v0);
-        }
-    }
+    };
+    if (GATHER && fm) main_loop(issue_fm);
+    else main_loop(issue_nat);
 
     const float l_tot = pair_sum(l_run);
     if (q_row < a.N) {
