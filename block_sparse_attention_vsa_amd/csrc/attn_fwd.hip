@@ -63,12 +63,6 @@ __device__ __forceinline__ int fm_natural(const AttnArgs& a, int r) {
     return (int)(((uint32_t)r - s * (uint32_t)a.T) * (uint32_t)a.HW + s);
 }
 
-__device__ __forceinline__ int xcd_remap(int bid, int G) {
-    // Workgroup `bid` runs on XCD bid % 8; give each XCD a contiguous item range.
-    int x = bid & 7, j = bid >> 3;
-    int q = G >> 3, r = G & 7;
-    return x * q + min(x, r) + j;
-}
 
 __device__ __forceinline__ int block_valid(const int32_t* blk_len, int b, int BS, int N) {
     int exist = min(BS, N - b * BS);

@@ -186,13 +186,24 @@ __device__ __forceinline__ uint32_t buf_load_u32(const void* base, int nbytes, i
     return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
 }
 
-template <int WAVES>
+// V swizzles: kVSwz4 puts chunk c of row r at slot c ^ 4 (r & 3) (for the 32x32
+// operand reads of the attention kernel); kVSwzPair at slot c ^ 2 (r & 7), i.e.
+// 32-byte pair q at pair q ^ (r & 7) (for the 16x16 operand reads of the
+// profiler). Either way the transposing reads touch every bank the minimum
+// number of times.
+enum { kVSwz4 = 0, kVSwzPair = 1 };
+__device__ __forceinline__ int v_swizzle(int vswz, int row) {
+    return vswz == kVSwz4 ? 4 * (row & 3) : 2 * (row & 7);
+}
+
+template <int WAVES, int VSWZ = kVSwz4>
 struct SubTileDma {
     static constexpr int IPW = kSubBytes / 1024 / WAVES;   // wave instructions per tensor per sub-tile
     // Instruction u covers rows 4 (w + WAVES u) + (lane >> 4). Bits 0..3 of the
     // row, which pick the K swizzle, repeat every NCLS instructions (once for 4
-    // waves); bits 0..1, which pick the V swizzle, never change with u.
+    // waves); the V swizzle's bits (0..1, or 0..2 with 4 waves) never change with u.
     static constexpr int NCLS = (4 * WAVES >= 16) ? 1 : 16 / (4 * WAVES);
+    static_assert(VSWZ == kVSwz4 || WAVES >= 2, "pair swizzle needs u-independent row bits 0..2");
     int rowb;                       // byte offset of this lane's row for u = 0
     int ck[NCLS], cv;               // swizzled chunk offsets (bytes)
     __device__ __forceinline__ SubTileDma(int lane, int w) {
@@ -203,7 +214,7 @@ struct SubTileDma {
             const int row = 4 * (w + WAVES * u) + (lane >> 4);
             ck[u] = (p ^ (row & 15)) << 4;
         }
-        cv = (p ^ (4 * ((lane >> 4) & 3))) << 4;
+        cv = (p ^ v_swizzle(VSWZ, 4 * w + (lane >> 4))) << 4;
     }
     __device__ __forceinline__ int voff_k(int u) const { return rowb + 1024 * WAVES * u + ck[u % NCLS]; }
     __device__ __forceinline__ int voff_v(int u) const { return rowb + 1024 * WAVES * u + cv; }

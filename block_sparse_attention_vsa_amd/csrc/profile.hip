@@ -10,9 +10,9 @@
 //     set iff M_p[L_p(r) / bs][L_p(n) / bs] != 0, where L_p is the identity
 //     (mask stated in natural order) or the frame-major map (n -> s*T + t).
 //  2. main (one launch for the dense output and up to two candidates):
-//     workgroups of 4 waves cover 64 sampled rows; waves 0/1 and 2/3 take the
-//     two 32-row groups, and within a group each wave owns one half of the
-//     output channels, so three output sets fit 2 waves per SIMD. Each
+//     workgroups of 4 waves cover 64 sampled rows, 16 per wave, on the
+//     16x16x32 bf16 MFMA (scores and P V), so three output sets over all 128
+//     channels fit 2 waves per SIMD and no score is computed twice. Each
 //     workgroup walks a contiguous range of 64-key sub-tiles (split-K over
 //     keys, so a few hundred rows still fill the chip), with K and V streamed
 //     into double-buffered LDS by DMA and the candidates' bit words fetched one
@@ -85,23 +85,27 @@ __device__ __forceinline__ uint32_t layout_pos(const BitsArgs& a, int lay, uint3
     return (n - t * a.HW) * a.T + t;        // frame-major position of natural token n
 }
 
+// One thread per 32-key word; the 32 key positions are computed independently
+// (fully unrolled), so the 32 mask-byte loads are in flight together.
 __global__ __launch_bounds__(256) void prof_bits_kernel(BitsArgs a) {
-    int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    int64_t total = (int64_t)a.P * a.R * a.words;
+    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t total = (int64_t)a.P * a.R * a.words;
     if (e >= total) return;
-    int wi = (int)(e % a.words);
-    int64_t pr = e / a.words;
-    int ri = (int)(pr % a.R);
-    int p = (int)(pr / a.R);
-    int r = a.rows[ri];
+    const int wi = (int)(e % a.words);
+    const int64_t pr = e / a.words;
+    const int ri = (int)(pr % a.R);
+    const int p = (int)(pr / a.R);
+    const int r = a.rows[ri];
     uint32_t word = 0;
-    if (r >= 0 && r < a.N) {
-        int lay = a.layout[p];
-        uint32_t qblk = a.div_bs.div(layout_pos(a, lay, (uint32_t)r));
+    if (r >= 0 && r < a.N && 32 * wi < a.N) {
+        const int lay = a.layout[p];
+        const uint32_t qblk = a.div_bs.div(layout_pos(a, lay, (uint32_t)r));
         const uint8_t* mrow = a.masks + ((int64_t)p * a.nb + qblk) * a.nb;
+#pragma unroll
         for (int b = 0; b < 32; ++b) {
-            int n = 32 * wi + b;
-            if (n < a.N && mrow[a.div_bs.div(layout_pos(a, lay, (uint32_t)n))]) word |= 1u << b;
+            const uint32_t n = (uint32_t)min(32 * wi + b, a.N - 1);      // clamped: loaded, then dropped
+            const uint8_t m = mrow[a.div_bs.div(layout_pos(a, lay, n))];
+            if (m && 32 * wi + b < a.N) word |= 1u << b;
         }
     }
     a.bits[e] = word;
@@ -122,9 +126,74 @@ struct ProfArgs {
     int32_t cand[kProfCandPerLaunch];    // candidates handled (slot 1 + cand), -1 = none
 };
 
+// Sum / max over the four 16-lane groups of a wave (one query per lane n & 15,
+// its keys spread over the groups), in a fixed order: every group ends with the
+// same bits.
+__device__ __forceinline__ float group4_max(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    const float y = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+    return fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
+}
+__device__ __forceinline__ float group4_sum(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    const float y = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+    return __uint_as_float(q[0]) + __uint_as_float(q[1]);
+}
+
+// LDS addressing of the 16x16x32 operands, written as a per-lane base plus
+// terms that are immediates or one XOR, so only a few address registers stay
+// live across the loop.
+//  K (row r at r * 256, chunk c at slot c ^ (r & 15)): the A operand of S^T
+//    for key tile tt and channel step kk reads row 16 tt + n, chunk 4 kk + g:
+//    byte 4096 tt + ka[kk], ka[kk] = 256 n + 16 (g ^ (n & 3)) + 16 (4 kk ^ (n & 12)).
+//  V (pair swizzle: 32-byte pair q of row r at pair q ^ (r & 7)): the V^T
+//    operand of P V for channel tile ct (16 channels) and K-step j is two
+//    ds_read_b64_tr_b16. The P^T operand of lane group g holds keys
+//    32 j + 4 g + [0, 4) (elements 0..3) and 32 j + 16 + 4 g + [0, 4)
+//    (elements 4..7), which is how the 16x16 score accumulators hold them; in
+//    each 16-lane group, lanes 4 jj .. 4 jj + 3 point at 16 consecutive
+//    channels of key jj and lane i receives channel i of the four keys. The
+//    byte address is 8192 j + 4096 h + va[ct], va[ct] = vbase ^ 32 ct, with
+//    vbase = 256 (4 g + n / 4) + 16 ((n & 3) >> 1) + 8 (n & 1) + 32 ((4 g + n / 4) & 7).
+// The per-lane parts are passed through an empty asm so the compiler cannot
+// see that their bits are disjoint from the constant parts: it then keeps
+// base + constant as an add, which folds into the instruction's offset field,
+// instead of an OR that needs a register per address.
+struct Op16Addr {
+    int ka[4], va[8];               // K: kbase + kx[kk]; V: vbase ^ 32 ct
+    __device__ __forceinline__ explicit Op16Addr(int lane) {
+        const int g = lane >> 4, n = lane & 15;
+        const int kbase = 256 * n + 16 * (g ^ (n & 3));
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            ka[kk] = kbase + 16 * ((4 * kk) ^ (n & 12));
+            asm("" : "+v"(ka[kk]));
+        }
+        const int krow = 4 * g + (n >> 2);     // key row of this lane within a 16-key run
+        const int vbase = 256 * krow + 16 * ((n & 3) >> 1) + 8 * (n & 1) + 32 * (krow & 7);
+#pragma unroll
+        for (int ct = 0; ct < 8; ++ct) {
+            va[ct] = vbase ^ (32 * ct);
+            asm("" : "+v"(va[ct]));
+        }
+    }
+};
+
+__device__ __forceinline__ bf16x8 vt_operand16(const uint8_t* vt, int ct, int j, const Op16Addr& ad) {
+    v4i16 part[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const uint8_t* ptr = vt + 8192 * j + 4096 * h + ad.va[ct];
+        part[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(ptr));
+    }
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
 template <int NCAND>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void prof_main_kernel(ProfArgs a) {
-    constexpr int D = 128, KT = kSubKeys, NS = 1 + NCAND;
+    constexpr int D = 128, KT = kSubKeys, NS = 1 + NCAND, NCT = D / 16;
     constexpr float TAU = 8.f;
     // two stages as distinct LDS objects, loop unrolled by two: a DMA into one
     // stage is then provably disjoint from reads of the other
@@ -132,30 +201,45 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     __shared__ __attribute__((aligned(1024))) uint8_t v0[kSubBytes];
     __shared__ __attribute__((aligned(1024))) uint8_t k1[kSubBytes];
     __shared__ __attribute__((aligned(1024))) uint8_t v1[kSubBytes];
+    // the workgroup's 64 query rows, K-style swizzle (chunk c of row r at slot c ^ (r & 15)):
+    // the Q^T operands are read back just before the scores, so they hold no
+    // registers across the P V products
+    __shared__ __attribute__((aligned(1024))) uint8_t qs[kProfRows * D * 2];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int l32 = lane & 31, half = lane >> 5;
-    const int rg = w & 1, chh = w >> 1;             // row group, channel half
-    const int split = blockIdx.x, rt = blockIdx.y, bh = blockIdx.z;
+    const int n16 = lane & 15, g = lane >> 4;     // query of this lane, its key group
+    // Workgroups are dealt round-robin over the 8 XCDs; the item order gives
+    // each XCD a contiguous range of (b h, split) groups with their row tiles
+    // fastest, so the row tiles that stream the same K/V range share one L2.
+    const int RTn = (a.R + kProfRows - 1) / kProfRows;
+    const int item = xcd_remap((int)blockIdx.x, a.S * RTn * a.BH);
+    const int rt = item % RTn, split = (item / RTn) % a.S, bh = item / (RTn * a.S);
     const int64_t head_off = (int64_t)bh * a.N * D;
-    const int ri = rt * kProfRows + 32 * rg + l32;
+    const int ri = rt * kProfRows + 16 * w + n16;
     const int r = ri < a.R ? a.rows[ri] : -1;
     const bool row_ok = r >= 0 && r < a.N;
-    const bool wave_active = rt * kProfRows + 32 * rg < a.R;
+    const bool wave_active = rt * kProfRows + 16 * w < a.R;
 
-    bf16x8 qf[D / 16];
-    load_q_frag<D>(qf, a.q + head_off + (int64_t)(row_ok ? r : 0) * D, row_ok, half);
+    const Op16Addr ad(lane);
+    // Q^T operand per 32-channel step kk (channels 32 kk + 8 g .. + 8 of this
+    // lane's row) staged in LDS at the same swizzled spot the K operand uses
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk) {
+        u32x4 t = {0u, 0u, 0u, 0u};
+        if (row_ok) t = *reinterpret_cast<const u32x4*>(a.q + head_off + (int64_t)r * D + 32 * kk + 8 * g);
+        *reinterpret_cast<u32x4*>(qs + 4096 * w + ad.ka[kk]) = t;
+    }
 
-    f32x16 o[NS][2];                 // channel tiles 2 chh, 2 chh + 1 of every set
+    f32x4 o[NS][NCT];                // O^T tiles: channels 16 ct + 4 g + i, query n16
     float l_run[NS];
     float m_run = -INFINITY;         // running offset shared by all sets
 #pragma unroll
     for (int c = 0; c < NS; ++c) {
         l_run[c] = 0.f;
-        o[c][0] = f32x16{};
-        o[c][1] = f32x16{};
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) o[c][ct] = f32x4{};
     }
     const int t0 = split * a.TPS, t1 = min(t0 + a.TPS, a.nsub);
-    const SubTileDma<4> dma(lane, w);
+    const SubTileDma<4, kVSwzPair> dma(lane, w);
     const int head_bytes = a.N * D * 2;
     auto issue = [&](int t, uint8_t* kd, uint8_t* vd) {
         dma.issue(kd, vd, a.k + head_off, a.v + head_off, head_bytes, t * KT, w);
@@ -174,35 +258,40 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
             for (int st = 0; st < 2; ++st) wb[c][st] = buf_load_u32(a.bits, a.bits_bytes, boff[c], (2 * t + st) * 4);
     };
     uint32_t bits_cur[NCAND][2], bits_next[NCAND][2];
-    auto pv = [&](f32x16 (&oc)[2], const bf16x8 (&pf)[2][2], const uint8_t* vt) {
-#pragma unroll
-        for (int dl = 0; dl < 2; ++dl)
-#pragma unroll
-            for (int st = 0; st < 2; ++st)
-#pragma unroll
-                for (int g = 0; g < 2; ++g)
-                    oc[dl] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sub_vt_operand(vt, 2 * chh + dl, st, g, lane),
-                                                                     pf[st][g], oc[dl], 0, 0, 0);
-    };
-    auto compute = [&](int t, const uint8_t* kt, const uint8_t* vt) {
+
+    auto compute = [&](int t, const uint8_t* kt, const uint8_t* vt) __attribute__((always_inline)) {
         if (!wave_active) return;
         const int vs = min(KT, a.N - t * KT);
-        f32x16 s[2];
-        sub_scores(s, kt, qf, l32, half);
+        // S^T tiles: s[tt][i] = score of key 16 tt + 4 g + i for query n16
+        bf16x8 qf[D / 32];
+#pragma unroll
+        for (int kk = 0; kk < D / 32; ++kk)
+            qf[kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qs + 4096 * w + ad.ka[kk]));
+        f32x4 s[4];
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+            s[tt] = f32x4{};
+#pragma unroll
+            for (int kk = 0; kk < D / 32; ++kk) {
+                u32x4 kv = *reinterpret_cast<const u32x4*>(kt + 4096 * tt + ad.ka[kk]);
+                s[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kv), qf[kk], s[tt], 0, 0, 0);
+            }
+        }
         if (vs < KT) {
+            const int lim = vs - 4 * g;            // key 16 tt + 4 g + i is valid iff 16 tt + i < lim
 #pragma unroll
-            for (int st = 0; st < 2; ++st)
+            for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
-                for (int x = 0; x < 16; ++x)
-                    if (acc_key(st, x, half) >= vs) s[st][x] = -INFINITY;
+                for (int i = 0; i < 4; ++i)
+                    if (16 * tt + i >= lim) s[tt][i] = -INFINITY;
         }
         // dense online softmax; its offset serves every set
         float mx = -INFINITY;
 #pragma unroll
-        for (int st = 0; st < 2; ++st)
+        for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
-            for (int x = 0; x < 16; ++x) mx = fmaxf(mx, s[st][x]);
-        mx = pair_max(mx);
+            for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[tt][i]);
+        mx = group4_max(mx);
         const float m_tile = mx * a.scale_log2;
         const bool upd = m_tile > m_run + TAU;
         const float m_new = upd ? m_tile : m_run;
@@ -213,26 +302,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
             for (int c = 0; c < NS; ++c) {
                 l_run[c] *= alpha;
 #pragma unroll
-                for (int dl = 0; dl < 2; ++dl)
-#pragma unroll
-                    for (int x = 0; x < 16; ++x) o[c][dl][x] *= alpha;
+                for (int ct = 0; ct < NCT; ++ct) o[c][ct] *= alpha;
             }
         }
         m_run = m_new;
-        float ps[2] = {0.f, 0.f};
+        float ps[2] = {0.f, 0.f};              // per 32-key word: tiles 0, 1 and 2, 3
 #pragma unroll
-        for (int st = 0; st < 2; ++st)
+        for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
-            for (int x = 0; x < 16; ++x) {
-                s[st][x] = __builtin_amdgcn_exp2f(fmaf(s[st][x], a.scale_log2, -m_use));   // p, in place
-                ps[st] += s[st][x];
+            for (int i = 0; i < 4; ++i) {
+                s[tt][i] = __builtin_amdgcn_exp2f(fmaf(s[tt][i], a.scale_log2, -m_use));   // p, in place
+                ps[tt >> 1] += s[tt][i];
             }
         l_run[0] += ps[0] + ps[1];
-        // Candidates: none of the wave's rows keeps a key here -> skipped; every
-        // lane's words all-kept or all-dropped (block-aligned masks) -> the dense
-        // bf16 P with dropped lanes zeroed, after the dense P V; otherwise (keys
-        // kept one by one) P from the fp32 values first, so that those die
-        // before the dense bf16 copy exists.
+        // P^T operands for K-steps j = 0, 1: element e of lane group g is key
+        // 32 j + 16 (e >> 2) + 4 g + (e & 3), held in s[2 j + (e >> 2)][e & 3];
+        // its bit in the candidate's word j is 16 (e >> 2) + 4 g + (e & 3)
         bool any[NCAND], whole[NCAND];
 #pragma unroll
         for (int c = 0; c < NCAND; ++c) {
@@ -240,45 +325,54 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
             any[c] = __ballot((b0 | b1) != 0u) != 0;
             whole[c] = __ballot((b0 + 1u > 1u) || (b1 + 1u > 1u)) == 0;
         }
+        bf16x8 pc[NCAND][2];
+        // candidates kept key by key first, from the fp32 p
 #pragma unroll
         for (int c = 0; c < NCAND; ++c) {
             if (!any[c] || whole[c]) continue;
-            bf16x8 pc[2][2];
             float lc = 0.f;
 #pragma unroll
-            for (int st = 0; st < 2; ++st) {
-                const uint32_t wb = bits_cur[c][st];
+            for (int j = 0; j < 2; ++j) {
+                const uint32_t wb = bits_cur[c][j];
 #pragma unroll
-                for (int x = 0; x < 16; ++x) {
-                    const bool keep = (wb >> (8 * (x >> 2) + 4 * half + (x & 3))) & 1u;
-                    const float pk = keep ? s[st][x] : 0.f;
+                for (int e = 0; e < 8; ++e) {
+                    const bool keep = (wb >> (16 * (e >> 2) + 4 * g + (e & 3))) & 1u;
+                    const float pk = keep ? s[2 * j + (e >> 2)][e & 3] : 0.f;
                     lc += pk;
-                    pc[st][x >> 3][x & 7] = (__bf16)pk;
+                    pc[c][j][e] = (__bf16)pk;
                 }
             }
             l_run[1 + c] += lc;
-            pv(o[1 + c], pc, vt);
         }
-        bf16x8 pf[2][2];
+        bf16x8 pf[2];
 #pragma unroll
-        for (int st = 0; st < 2; ++st)
+        for (int j = 0; j < 2; ++j)
 #pragma unroll
-            for (int x = 0; x < 16; ++x) pf[st][x >> 3][x & 7] = (__bf16)s[st][x];
-        if (a.write_dense) pv(o[0], pf, vt);
+            for (int e = 0; e < 8; ++e) pf[j][e] = (__bf16)s[2 * j + (e >> 2)][e & 3];
+        // block-aligned candidates: the dense P with dropped lanes zeroed; a
+        // candidate no row of the wave keeps here gets P = 0
 #pragma unroll
         for (int c = 0; c < NCAND; ++c) {
-            if (!any[c] || !whole[c]) continue;
-            const uint32_t b0 = bits_cur[c][0], b1 = bits_cur[c][1];
+            if (any[c] && !whole[c]) continue;
             const bf16x8 zero = bf16x8{};
-            bf16x8 pc[2][2];
 #pragma unroll
-            for (int g = 0; g < 2; ++g) {
-                pc[0][g] = b0 ? pf[0][g] : zero;
-                pc[1][g] = b1 ? pf[1][g] : zero;
-            }
-            l_run[1 + c] += (b0 ? ps[0] : 0.f) + (b1 ? ps[1] : 0.f);
-            pv(o[1 + c], pc, vt);
+            for (int j = 0; j < 2; ++j) pc[c][j] = bits_cur[c][j] ? pf[j] : zero;
+            l_run[1 + c] += (bits_cur[c][0] ? ps[0] : 0.f) + (bits_cur[c][1] ? ps[1] : 0.f);
         }
+        // P V: each V^T operand feeds every set (a candidate's zero P adds
+        // nothing; the matrix cores are not this kernel's bottleneck)
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const bf16x8 va = vt_operand16(vt, ct, j, ad);
+                if (a.write_dense) o[0][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pf[j], o[0][ct], 0, 0, 0);
+#pragma unroll
+                for (int c = 0; c < NCAND; ++c)
+                    o[1 + c][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pc[c][j], o[1 + c][ct], 0, 0, 0);
+                // keep at most a few operand reads in flight (registers)
+
+            }
     };
     auto rotate = [&]() {
 #pragma unroll
@@ -317,21 +411,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
 #pragma unroll
     for (int c = 0; c < NS; ++c) {
         if (c == 0 && !a.write_dense) continue;
-        const float l_tot = pair_sum(l_run[c]);
+        const float l_tot = group4_sum(l_run[c]);
         if (ri >= a.R) continue;
         const int slot = c == 0 ? 0 : 1 + a.cand[c - 1];
         float* rec = a.part + ((((int64_t)slot * a.BH + bh) * a.R + ri) * a.S + split) * a.rec;
-        if (chh == 0 && half == 0) {
+        if (g == 0) {
             rec[0] = m_run;
             rec[1] = l_tot;
         }
 #pragma unroll
-        for (int dl = 0; dl < 2; ++dl)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                f32x4 v4 = {o[c][dl][4 * j], o[c][dl][4 * j + 1], o[c][dl][4 * j + 2], o[c][dl][4 * j + 3]};
-                *reinterpret_cast<f32x4*>(rec + 4 + 32 * (2 * chh + dl) + 8 * j + 4 * half) = v4;
-            }
+        for (int ct = 0; ct < NCT; ++ct) *reinterpret_cast<f32x4*>(rec + 4 + 16 * ct + 4 * g) = o[c][ct];
     }
 }
 
@@ -343,7 +432,8 @@ struct MergeArgs {
 };
 
 // One workgroup of D = 128 threads per (b, h, sampled row); thread d merges
-// channel d of every slot over the splits in order.
+// channel d of every slot over the splits in order (exact log-sum-exp
+// rescaling).
 __global__ __launch_bounds__(128) void prof_merge_kernel(MergeArgs a) {
     __shared__ float red[kProfMaxP][128];
     const int ri = blockIdx.x, bh = blockIdx.y, d = threadIdx.x;
@@ -462,7 +552,7 @@ extern "C" int vsa_profile_heads(const void* q, const void* k, const void* v, in
     pa.BH = B * H; pa.rec = pl.rec;
     pa.bits_bytes = (int32_t)((size_t)P * R * pl.words * 4);
     pa.scale_log2 = (float)((double)scale * 1.4426950408889634);
-    dim3 grid(pl.S, pl.RT, B * H);
+    dim3 grid((unsigned)((int64_t)pl.S * pl.RT * B * H));
     // the dense set and up to two candidates per launch (S recomputed per launch)
     for (int first = 0; first < P; first += kProfCandPerLaunch) {
         const int nc = std::min(kProfCandPerLaunch, P - first);

@@ -54,4 +54,14 @@ struct FastDiv {
     }
 };
 
+// Workgroup `bid` of a G-workgroup grid runs on XCD bid % 8 (round-robin
+// dispatch over the 8 XCDs). Returns the item it should process so that each
+// XCD owns a contiguous range of items, [x q + min(x, r), ...) with q = G / 8,
+// r = G % 8: neighbouring items then share that XCD's L2. A bijection on [0, G).
+__device__ __forceinline__ int xcd_remap(int bid, int G) {
+    const int x = bid & 7, j = bid >> 3;
+    const int q = G >> 3, r = G & 7;
+    return x * q + min(x, r) + j;
+}
+
 }  // namespace vsa
