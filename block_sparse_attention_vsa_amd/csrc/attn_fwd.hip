@@ -250,18 +250,19 @@ __device__ __forceinline__ int block_valid_c(const int32_t* blk_len, int b, int 
 
 template <int BS, bool GATHER>
 __global__ __launch_bounds__(BS * 2) __attribute__((amdgpu_waves_per_eu(2))) void attn_fwd_bf16_d128_kernel(AttnArgs a) {
-    constexpr int D = 128, KT = 64;
+    // 128-row blocks walk 64-key sub-tiles (2 workgroups per CU); 64-row blocks
+    // walk 32-key sub-tiles, so that two stages still fit 4 workgroups per CU
+    constexpr int D = 128, KT = (BS == 128) ? 64 : 32, NST = KT / 32, SUBB = KT * D * 2;
     constexpr int WAVES = BS / 32, THREADS = WAVES * 64, SUB = BS / KT;
     constexpr float TAU = 8.f;
-
-    // 128-row blocks: two stages (2 workgroups per CU); 64-row blocks: one stage,
-    // so that 4 workgroups fit a CU and overlap each other's loads instead
-    constexpr bool TWO_STAGES = (BS == 128);
-    __shared__ __attribute__((aligned(1024))) uint8_t k0[kSubBytes];
-    __shared__ __attribute__((aligned(1024))) uint8_t v0[kSubBytes];
-    __shared__ __attribute__((aligned(1024))) uint8_t k1[TWO_STAGES ? kSubBytes : 16];
-    __shared__ __attribute__((aligned(1024))) uint8_t v1[TWO_STAGES ? kSubBytes : 16];
-    __shared__ int16_t list_lds[kMaxMaskBlocks];
+    constexpr bool TWO_STAGES = true;
+    __shared__ __attribute__((aligned(1024))) uint8_t k0[SUBB];
+    __shared__ __attribute__((aligned(1024))) uint8_t v0[SUBB];
+    __shared__ __attribute__((aligned(1024))) uint8_t k1[SUBB];
+    __shared__ __attribute__((aligned(1024))) uint8_t v1[SUBB];
+    // mask form only: the compacted row, sized at launch (0 bytes for the list
+    // form, so 64-row blocks fit 4 workgroups per CU)
+    extern __shared__ __attribute__((aligned(16))) int16_t list_lds[];
     __shared__ int wave_cnt[WAVES];
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -303,7 +304,7 @@ __global__ __launch_bounds__(BS * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
         int v = block_valid_c(a.blk_len, kb, BS, a.N) - (i % SUB) * KT;
         return v < 0 ? 0 : (v > KT ? KT : v);
     };
-    const SubTileDma<WAVES> dma(lane, w);
+    const SubTileDma<WAVES, kVSwz4, KT> dma(lane, w);
     const int head_bytes = a.N * D * 2;
     // natural rows / rows through the frame-major map; the main loop below is
     // instantiated once per form, so a natural head runs no gather code
@@ -336,12 +337,12 @@ __global__ __launch_bounds__(BS * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
         int kb;
         const int vs = sub_valid(i, kb);
         if (!wave_active || vs == 0) return;
-        // ---- S^T = K Q^T (2 x 32 keys) ----------------------------------------
-        f32x16 s[2];
-        sub_scores(s, kt, qf, l32, half);
+        // ---- S^T = K Q^T (NST x 32 keys) --------------------------------------
+        f32x16 s[NST];
+        sub_scores<NST>(s, kt, qf, l32, half);
         if (vs < KT) {
 #pragma unroll
-            for (int st = 0; st < 2; ++st)
+            for (int st = 0; st < NST; ++st)
 #pragma unroll
                 for (int x = 0; x < 16; ++x)
                     if (acc_key(st, x, half) >= vs) s[st][x] = -INFINITY;
@@ -349,7 +350,7 @@ __global__ __launch_bounds__(BS * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
         // ---- online softmax with a lazily moved offset ---------------------------
         float mx = -INFINITY;
 #pragma unroll
-        for (int st = 0; st < 2; ++st)
+        for (int st = 0; st < NST; ++st)
 #pragma unroll
             for (int x = 0; x < 16; ++x) mx = fmaxf(mx, s[st][x]);
         mx = pair_max(mx);
@@ -368,10 +369,10 @@ __global__ __launch_bounds__(BS * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
         m_run = m_new;
         // p in fp32 feeds the row sum (so the log-sum-exp keeps fp32 accuracy);
         // its bf16 rounding feeds the P V product
-        bf16x8 pf[2][2];
+        bf16x8 pf[NST][2];
         float ps[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int st = 0; st < 2; ++st)
+        for (int st = 0; st < NST; ++st)
 #pragma unroll
             for (int x = 0; x < 16; ++x) {
                 const float p = __builtin_amdgcn_exp2f(fmaf(s[st][x], a.scale_log2, -m_use));
@@ -383,7 +384,7 @@ __global__ __launch_bounds__(BS * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-            for (int st = 0; st < 2; ++st)
+            for (int st = 0; st < NST; ++st)
 #pragma unroll
                 for (int g = 0; g < 2; ++g)
                     o_acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sub_vt_operand(vt, dt, st, g, lane),
@@ -595,12 +596,13 @@ void launch_attn(const AttnArgs& a, int D, int dtype, int bs, hipStream_t s) {
         for (int i = 0; i < 32; ++i) gather |= a.fm_bits[i] != 0;
         if (a.head_choice)
             for (int c = 0; c < a.n_cand; ++c) gather |= a.cand_fm[c] != 0;
+        const size_t shm = a.mask ? (((size_t)a.nb * 2 + 15) & ~(size_t)15) : 0;
         if (D == 128 && bs == 128) {
-            if (gather) hipLaunchKernelGGL((attn_fwd_bf16_d128_kernel<128, true>), grid, dim3(256), 0, s, a);
-            else hipLaunchKernelGGL((attn_fwd_bf16_d128_kernel<128, false>), grid, dim3(256), 0, s, a);
+            if (gather) hipLaunchKernelGGL((attn_fwd_bf16_d128_kernel<128, true>), grid, dim3(256), shm, s, a);
+            else hipLaunchKernelGGL((attn_fwd_bf16_d128_kernel<128, false>), grid, dim3(256), shm, s, a);
         } else if (D == 128 && bs == 64) {
-            if (gather) hipLaunchKernelGGL((attn_fwd_bf16_d128_kernel<64, true>), grid, dim3(128), 0, s, a);
-            else hipLaunchKernelGGL((attn_fwd_bf16_d128_kernel<64, false>), grid, dim3(128), 0, s, a);
+            if (gather) hipLaunchKernelGGL((attn_fwd_bf16_d128_kernel<64, true>), grid, dim3(128), shm, s, a);
+            else hipLaunchKernelGGL((attn_fwd_bf16_d128_kernel<64, false>), grid, dim3(128), shm, s, a);
         }
         else if (D == 64 && bs == 128) hipLaunchKernelGGL((attn_fwd_bf16_kernel<64, 128>), grid, dim3(256), 0, s, a);
         else hipLaunchKernelGGL((attn_fwd_bf16_kernel<64, 64>), grid, dim3(128), 0, s, a);

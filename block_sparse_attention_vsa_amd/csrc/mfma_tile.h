@@ -196,9 +196,10 @@ __device__ __forceinline__ int v_swizzle(int vswz, int row) {
     return vswz == kVSwz4 ? 4 * (row & 3) : 2 * (row & 7);
 }
 
-template <int WAVES, int VSWZ = kVSwz4>
+template <int WAVES, int VSWZ = kVSwz4, int KEYS = kSubKeys>
 struct SubTileDma {
-    static constexpr int IPW = kSubBytes / 1024 / WAVES;   // wave instructions per tensor per sub-tile
+    static constexpr int IPW = KEYS * 256 / 1024 / WAVES;   // wave instructions per tensor per sub-tile
+    static_assert(IPW >= 1, "every wave issues at least one instruction per tensor");
     // Instruction u covers rows 4 (w + WAVES u) + (lane >> 4). Bits 0..3 of the
     // row, which pick the K swizzle, repeat every NCLS instructions (once for 4
     // waves); the V swizzle's bits (0..1, or 0..2 with 4 waves) never change with u.
@@ -249,12 +250,13 @@ struct SubTileDma {
     }
 };
 
-// S^T for a 64-key sub-tile: s[st] holds keys 32 st + acc_key(0, x, half).
-__device__ __forceinline__ void sub_scores(f32x16 (&s)[2], const uint8_t* kt, const bf16x8 (&qf)[8], int l32,
+// S^T for a sub-tile of 32 NST keys: s[st] holds keys 32 st + acc_key(0, x, half).
+template <int NST>
+__device__ __forceinline__ void sub_scores(f32x16 (&s)[NST], const uint8_t* kt, const bf16x8 (&qf)[8], int l32,
                                            int half) {
     constexpr int D = 128;
 #pragma unroll
-    for (int st = 0; st < 2; ++st) {
+    for (int st = 0; st < NST; ++st) {
         s[st] = f32x16{};
         const int r = 32 * st + l32;
 #pragma unroll
