@@ -61,6 +61,9 @@ _SIGNATURES = {
                                                 ctypes.POINTER(vsa_blocks), _F, _P]),
     "vsa_block_sparse_attn_fwd_chosen": (_I, [_P, _P, _P, _P, _P, _I, _I, vsa_grid, _I, _I, _I, _P, _P, _I, _P,
                                               _P, _F, _P]),
+    "vsa_attn_bwd_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I]),
+    "vsa_block_sparse_attn_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P,
+                                       ctypes.POINTER(vsa_blocks), _F, _P, _SZ, _P]),
     "vsa_check_block_list_host": (_I, [_P, _P, _I64, _I, _I]),
 }
 
@@ -410,6 +413,44 @@ def vsa_block_sparse_attn_fwd_chosen(q, k, v, grid, bs: int, cand_masks, cand_la
                                                   scale, _stream(q.device)),
            "vsa_block_sparse_attn_fwd_chosen")
     return (out, lse) if return_lse else out
+
+
+def vsa_attn_bwd_workspace_bytes(B, H, N, bs, list_form) -> int:
+    return lib().vsa_attn_bwd_workspace_bytes(B, H, N, bs, int(bool(list_form)))
+
+
+def vsa_block_sparse_attn_bwd(q, k, v, o, lse, dout, bs: int, mask=None, kv_idx=None, kv_cnt=None, blk_len=None,
+                              scale=None, dq=None, dk=None, dv=None, workspace=None):
+    """(dq, dk, dv) of the forward with the same block set; o and lse are the
+    forward's outputs, dout the upstream gradient."""
+    torch = _torch()
+    _need(q, "q", ndim=4)
+    for t, name in ((k, "k"), (v, "v"), (o, "o"), (dout, "dout")):
+        _need(t, name, q.dtype, 4)
+        if t.shape != q.shape:
+            raise ValueError(f"{name} must have the shape of q")
+    B, H, N, D = q.shape
+    _need(lse, "lse", torch.float32, 3)
+    if tuple(lse.shape) != (B, H, N):
+        raise ValueError("lse must be [B, H, N]")
+    if blk_len is not None:
+        _need(blk_len, "blk_len", torch.int32, 1)
+    scale = default_scale(D) if scale is None else scale
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    for t, name in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
+        _need(t, name, q.dtype, 4)
+    blocks = _blocks_arg(q, bs, mask, kv_idx, kv_cnt)
+    ws = vsa_attn_bwd_workspace_bytes(B, H, N, bs, kv_idx is not None)
+    if workspace is None and ws:
+        workspace = torch.empty((ws,), dtype=torch.uint8, device=q.device)
+    _check(lib().vsa_block_sparse_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq),
+                                           _ptr(dk), _ptr(dv), B, H, N, D, _dtype_code(q), bs, _ptr(blk_len),
+                                           ctypes.byref(blocks), scale, _ptr(workspace),
+                                           0 if workspace is None else workspace.numel(), _stream(q.device)),
+           "vsa_block_sparse_attn_bwd")
+    return dq, dk, dv
 
 
 def vsa_check_block_list_host(kv_idx: np.ndarray, kv_cnt: np.ndarray, nkb: int) -> None:

@@ -19,7 +19,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libvsa.so")
 
-SOURCES = ["status.hip", "pattern.hip", "permute.hip", "attn_fwd.hip", "scores.hip", "select.hip",
+SOURCES = ["status.hip", "pattern.hip", "permute.hip", "attn_fwd.hip", "attn_bwd.hip", "scores.hip", "select.hip",
            "profile.hip"]
 
 ARCH = "gfx950"

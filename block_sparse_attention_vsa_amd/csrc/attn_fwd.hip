@@ -69,32 +69,6 @@ __device__ __forceinline__ int block_valid(const int32_t* blk_len, int b, int BS
     return blk_len ? min(blk_len[b], exist) : exist;
 }
 
-// Builds this workgroup's ascending list of kept key blocks from a mask row.
-template <int THREADS>
-__device__ int compact_mask_row(const uint8_t* row, int nkb, int16_t* list, int* wave_cnt) {
-    constexpr int WAVES = THREADS / 64;
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    int base = 0;
-    for (int r0 = 0; r0 < nkb; r0 += THREADS) {
-        int e = r0 + threadIdx.x;
-        bool keep = e < nkb && row[e] != 0;
-        uint64_t bal = __ballot(keep);
-        if (lane == 0) wave_cnt[w] = __popcll(bal);
-        __syncthreads();
-        int before = 0, total = 0;
-#pragma unroll
-        for (int i = 0; i < WAVES; ++i) {
-            int c = wave_cnt[i];
-            before += (i < w) ? c : 0;
-            total += c;
-        }
-        if (keep) list[base + before + __popcll(bal & ((1ull << lane) - 1ull))] = (int16_t)e;
-        base += total;
-        __syncthreads();
-    }
-    return base;
-}
-
 template <int D, int BS>
 __global__ __launch_bounds__(BS * 2) void attn_fwd_bf16_kernel(AttnArgs a) {
     constexpr int WAVES = BS / 32;
@@ -240,9 +214,6 @@ __global__ __launch_bounds__(BS * 2) void attn_fwd_bf16_kernel(AttnArgs a) {
 //  * Softmax keeps a running offset m per query that only moves when a tile's
 //    max exceeds it by more than 8 (log2 units), so O is rarely rescaled; p stays
 //    below 2^8 and the final O / l is unchanged.
-__device__ __forceinline__ int32_t ld_const(const int32_t* p, int64_t i) {
-    return ((const __attribute__((address_space(4))) int32_t*)p)[i];
-}
 __device__ __forceinline__ int block_valid_c(const int32_t* blk_len, int b, int BS, int N) {
     int exist = min(BS, N - b * BS);
     return blk_len ? min(ld_const(blk_len, b), exist) : exist;

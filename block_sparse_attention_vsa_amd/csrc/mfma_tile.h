@@ -178,6 +178,39 @@ __device__ __forceinline__ void dma16(const void* base, int nbytes, void* lds_ds
                                              0);
 }
 
+// Load of a wave-uniform int32 through the constant address space: a scalar
+// load, waited on with lgkmcnt, so it never waits for vector-memory traffic
+// such as the LDS DMA.
+__device__ __forceinline__ int32_t ld_const(const int32_t* p, int64_t i) {
+    return ((const __attribute__((address_space(4))) int32_t*)p)[i];
+}
+
+// Builds this workgroup's ascending list of kept key blocks from a mask row.
+template <int THREADS>
+__device__ int compact_mask_row(const uint8_t* row, int nkb, int16_t* list, int* wave_cnt) {
+    constexpr int WAVES = THREADS / 64;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    int base = 0;
+    for (int r0 = 0; r0 < nkb; r0 += THREADS) {
+        int e = r0 + threadIdx.x;
+        bool keep = e < nkb && row[e] != 0;
+        uint64_t bal = __ballot(keep);
+        if (lane == 0) wave_cnt[w] = __popcll(bal);
+        __syncthreads();
+        int before = 0, total = 0;
+#pragma unroll
+        for (int i = 0; i < WAVES; ++i) {
+            int c = wave_cnt[i];
+            before += (i < w) ? c : 0;
+            total += c;
+        }
+        if (keep) list[base + before + __popcll(bal & ((1ull << lane) - 1ull))] = (int16_t)e;
+        base += total;
+        __syncthreads();
+    }
+    return base;
+}
+
 // One dword through a buffer descriptor spanning nbytes: an offset voff at or
 // past nbytes reads 0 (the per-lane offset is range checked).
 __device__ __forceinline__ uint32_t buf_load_u32(const void* base, int nbytes, int voff, int soff) {
@@ -282,6 +315,161 @@ __device__ __forceinline__ bf16x8 sub_vt_operand(const uint8_t* vt, int dt, int 
     for (int r2 = 0; r2 < 2; ++r2) {
         const int key = 32 * st + 16 * g + 8 * r2 + 4 * (G >> 1) + j;
         const uint8_t* ptr = vt + key * D * 2 + ((chunk ^ (4 * (key & 3))) << 4) + (c & 1) * 8;
+        part[r2] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(ptr));
+    }
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+}  // namespace vsa
+
+namespace vsa {
+
+// ---------------------------------------------------------------------------
+// Generic tile access for kernels that read one staged tile both ways.
+//
+// A staged tile is rows of 128 bf16 (256 bytes, 16 chunks of 16 bytes); chunk c
+// of row r sits at slot c ^ swz(r). Two access patterns read it:
+//  * row operand (32x32x16 A operand, or B operand from rows): lane l reads row
+//    32 st + (l & 31), chunk 2 kk + (l >> 5), 16 bytes (ds_read_b128);
+//  * transposed operand (the V^T pattern above): two ds_read_b64_tr_b16.
+// kSwzRows (r & 15) is conflict-free for the first, kSwzTr (4 (r & 3)) for the
+// second, and kSwzBoth ((r & 3) << 2 | (r >> 2) & 3, the two 2-bit halves of
+// r & 15 swapped) for both; a bank model of 64 four-byte banks with 16 lanes per
+// ds_read_b128 phase and 32 per ds_read_b64 phase shows each pass touches
+// every bank once.
+enum { kSwzRows = 0, kSwzTr = 1, kSwzBoth = 2 };
+
+template <int SWZ>
+__device__ __forceinline__ int tile_swizzle(int r) {
+    if constexpr (SWZ == kSwzRows) return r & 15;
+    else if constexpr (SWZ == kSwzTr) return 4 * (r & 3);
+    else return ((r & 3) << 2) | ((r >> 2) & 3);
+}
+
+// DMA of a KEYS-row sub-tile of two tensors (A with swizzle SA, B with SB) into
+// LDS; same lane/instruction mapping as SubTileDma. Rows past the head's end
+// read as zeros (the whole row offset is in the range-checked lane offset).
+template <int WAVES, int SA, int SB, int KEYS>
+struct PairTileDma {
+    static constexpr int IPW = KEYS * 256 / 1024 / WAVES;
+    static_assert(IPW >= 1, "every wave issues at least one instruction per tensor");
+    static constexpr int NCLS = (4 * WAVES >= 16) ? 1 : 16 / (4 * WAVES);   // swizzle classes over u
+    int rowb, ca[NCLS], cb[NCLS];
+    __device__ __forceinline__ PairTileDma(int lane, int w) {
+        const int p = lane & 15;
+        rowb = (4 * w + (lane >> 4)) * 256;
+#pragma unroll
+        for (int u = 0; u < NCLS; ++u) {
+            const int row = 4 * (w + WAVES * u) + (lane >> 4);
+            ca[u] = (p ^ tile_swizzle<SA>(row)) << 4;
+            cb[u] = (p ^ tile_swizzle<SB>(row)) << 4;
+        }
+    }
+    __device__ __forceinline__ void issue(uint8_t* a_dst, uint8_t* b_dst, const uint16_t* a_head,
+                                          const uint16_t* b_head, int head_bytes, int row0, int w) const {
+        const int base = row0 * 256;
+#pragma unroll
+        for (int u = 0; u < IPW; ++u) {
+            const int ins = w + WAVES * u;
+            const int off = base + rowb + 1024 * WAVES * u;
+            dma16(a_head, head_bytes, a_dst + ins * 1024, off + ca[u % NCLS], 0);
+            dma16(b_head, head_bytes, b_dst + ins * 1024, off + cb[u % NCLS], 0);
+        }
+    }
+};
+
+// s[st] += A(rows of the tile) x B(frag): for st < NST, the 32x32 products over
+// the 128 channels; rows 32 st + (lane & 31) of the tile are the M index and the
+// fragment's 32 lanes the N index.
+template <int NST, int SWZ>
+__device__ __forceinline__ void tile_rows_mma(f32x16 (&s)[NST], const uint8_t* tile, const bf16x8 (&frag)[8],
+                                              int l32, int half) {
+#pragma unroll
+    for (int st = 0; st < NST; ++st) {
+        s[st] = f32x16{};
+        const int r = 32 * st + l32;
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) {
+            u32x4 t = *reinterpret_cast<const u32x4*>(tile + r * 256 + (((2 * kk + half) ^ tile_swizzle<SWZ>(r)) << 4));
+            s[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, t), frag[kk], s[st], 0, 0, 0);
+        }
+    }
+}
+
+// Transposed operand (channels 32 dt + (lane & 31) x the 16 rows of (st, g) in
+// the accumulator order) of a tile with swizzle SWZ; see sub_vt_operand.
+template <int SWZ>
+__device__ __forceinline__ bf16x8 tile_tr_operand(const uint8_t* tile, int dt, int st, int g, int lane) {
+    const int G = lane >> 4, gi = lane & 15;
+    const int j = gi >> 2, c = gi & 3;
+    const int chunk = 4 * dt + 2 * (G & 1) + (c >> 1);
+    v4i16 part[2];
+#pragma unroll
+    for (int r2 = 0; r2 < 2; ++r2) {
+        const int row = 32 * st + 16 * g + 8 * r2 + 4 * (G >> 1) + j;
+        const uint8_t* ptr = tile + row * 256 + ((chunk ^ tile_swizzle<SWZ>(row)) << 4) + (c & 1) * 8;
+        part[r2] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(ptr));
+    }
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+}  // namespace vsa
+
+namespace vsa {
+
+// Per-lane LDS offsets of the two access patterns for a tile with swizzle SWZ,
+// computed once. The row index of both patterns differs from the lane's base
+// row by multiples of 16 within a 32-row half, so the swizzle (a function of
+// row & 15) is fixed per lane; the 32-row half, the stage buffer and the g step
+// are then constants the instruction's offset field absorbs. The values pass
+// through an empty asm so the compiler cannot prove their bits disjoint from
+// those constants and turn the add into an OR (which would need one register
+// per address).
+template <int SWZ>
+struct TileAddr {
+    int rows[8];        // row operand, channel step kk: row l32, chunk 2 kk + half
+    int tr[4][2];       // transposed operand, channel tile dt, r2
+    __device__ __forceinline__ explicit TileAddr(int lane) {
+        const int l32 = lane & 31, half = lane >> 5;
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) {
+            rows[kk] = l32 * 256 + (((2 * kk + half) ^ tile_swizzle<SWZ>(l32)) << 4);
+            asm("" : "+v"(rows[kk]));
+        }
+        const int G = lane >> 4, gi = lane & 15;
+        const int j = gi >> 2, c = gi & 3;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+            for (int r2 = 0; r2 < 2; ++r2) {
+                const int row = 8 * r2 + 4 * (G >> 1) + j;
+                const int chunk = 4 * dt + 2 * (G & 1) + (c >> 1);
+                tr[dt][r2] = row * 256 + ((chunk ^ tile_swizzle<SWZ>(row)) << 4) + (c & 1) * 8;
+                asm("" : "+v"(tr[dt][r2]));
+            }
+    }
+};
+
+// s = rows 32 st + [0, 32) of the tile (A) times frag (B), over 128 channels.
+template <int SWZ>
+__device__ __forceinline__ f32x16 tile_rows_mma_at(const uint8_t* tile, int st, const bf16x8 (&frag)[8],
+                                                   const TileAddr<SWZ>& ad) {
+    f32x16 s = f32x16{};
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+        u32x4 t = *reinterpret_cast<const u32x4*>(tile + 8192 * st + ad.rows[kk]);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, t), frag[kk], s, 0, 0, 0);
+    }
+    return s;
+}
+
+template <int SWZ>
+__device__ __forceinline__ bf16x8 tile_tr_operand_at(const uint8_t* tile, int dt, int st, int g,
+                                                     const TileAddr<SWZ>& ad) {
+    v4i16 part[2];
+#pragma unroll
+    for (int r2 = 0; r2 < 2; ++r2) {
+        const uint8_t* ptr = tile + (32 * st + 16 * g) * 256 + ad.tr[dt][r2];
         part[r2] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(ptr));
     }
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7));

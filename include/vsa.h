@@ -262,6 +262,39 @@ int vsa_block_sparse_attn_fwd_chosen(const void* q, const void* k, const void* v
                                      const int32_t* choice, const int32_t* blk_len, float scale,
                                      void* stream);
 
+/* Block-sparse attention backward: dQ, dK, dV of vsa_block_sparse_attn_fwd.
+ * USV page, Abstract and Figure 2 caption (the sparse attention is trained end
+ * to end) and OSP-Next page, "Method" (sparse fine-tuning) need these
+ * gradients. With P_ij = exp(scale <q_i, k_j> - LSE_i) for j in J(i), 0 else:
+ *   dV_j = sum_i P_ij dO_i,   dS_ij = P_ij (<dO_i, v_j> - Delta_i),
+ *   Delta_i = <dO_i, O_i>,    dQ_i = scale sum_j dS_ij k_j,
+ *   dK_j = scale sum_i dS_ij q_i,
+ * every sum over the kept (query block, key block) tiles only.
+ *   q, k, v      [B, H, N, D] forward inputs; bf16, D = 128, bs 64 or 128
+ *                (otherwise VSA_ERR_UNSUPPORTED)
+ *   o, lse       the forward's O [B, H, N, D] and LSE (device fp32 [B, H, N],
+ *                natural log; -inf = a row that keeps nothing)
+ *   dout         upstream gradient dO [B, H, N, D], bf16
+ *   dq, dk, dv   out [B, H, N, D], bf16, each rounded once from fp32 sums; rows
+ *                of invalid (padding) positions and positions with nothing
+ *                kept are 0. Must not alias any input.
+ *   blk_len, blocks, scale as for the forward (same block set); a list row must
+ *                hold distinct entries (a repeated block would count twice in dQ
+ *                only); the mask form needs nb <= 4096
+ *   workspace    device, >= vsa_attn_bwd_workspace_bytes(B, H, N, bs, list_form)
+ *                bytes, 16-byte aligned, list_form = 1 for the (kv_idx, kv_cnt)
+ *                form; holds base-2 LSE and Delta per row, and per key block the
+ *                ascending list of query blocks that keep it
+ * Launch order on `stream`: row statistics, block transpose, dQ (one workgroup
+ * per query block), dV and dK (one workgroup per key block each). No atomics:
+ * results are bit-reproducible. */
+size_t vsa_attn_bwd_workspace_bytes(int B, int H, int N, int bs, int list_form);
+int vsa_block_sparse_attn_bwd(const void* q, const void* k, const void* v, const void* o,
+                              const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                              int B, int H, int N, int D, int dtype, int bs,
+                              const int32_t* blk_len, const vsa_blocks* blocks, float scale,
+                              void* workspace, size_t ws_bytes, void* stream);
+
 /* Validates a block list held in HOST memory: every kv_cnt in [0, max_kv], the
  * first kv_cnt entries of each row strictly ascending and inside [0, nkb).
  * Returns VSA_OK or VSA_ERR_INVALID (message names the first bad row). */

@@ -45,3 +45,21 @@ def assert_lse_close(got: np.ndarray, ref: np.ndarray, what: str, tol=LSE_MAX_AB
     if fin.any():
         d = np.abs(got[fin] - ref[fin]).max()
         assert d <= tol, f"{what}: lse max-abs {d:.3e} > {tol}"
+
+
+# Gradients: the kernels round P and dS to bf16 before their products and each
+# output once to bf16, and take Delta from the forward's bf16 O. Emulating those
+# roundings on random unit-scale inputs against the fp64 definition gives a
+# largest error of at most 5e-3 of the tensor's largest magnitude and a mean error
+# of about 2.3e-3 of its mean magnitude (8e-3 with 4x larger logits, where the
+# softmax is peaked); the bounds below leave about 3x room.
+GRAD_MAX_REL = 1.5e-2
+GRAD_MEAN_REL = 7e-3
+
+
+def assert_grad_close(got: np.ndarray, ref: np.ndarray, what: str, max_rel=GRAD_MAX_REL, mean_rel=GRAD_MEAN_REL):
+    d = np.abs(got - ref)
+    assert np.isfinite(got).all(), f"{what}: non-finite gradient"
+    big, avg = np.abs(ref).max(), np.abs(ref).mean()
+    assert d.max() <= max_rel * big, f"{what}: max-abs {d.max():.3e} > {max_rel} x {big:.3e}"
+    assert d.mean() <= mean_rel * avg, f"{what}: mean-abs {d.mean():.3e} > {mean_rel} x {avg:.3e}"

@@ -182,3 +182,37 @@ def test_check_block_list_host():
 
 def test_attn_workspace_is_not_needed():
     assert V.vsa_attn_workspace_bytes(1, 12, 32760, 128, 256) == 0
+
+
+def test_backward_validation_and_workspace_size():
+    L = V.lib()
+    fake = ctypes.c_void_p(0x1000)
+    blk = V.vsa_blocks()
+    blk.mask = 0x1000
+    # B=1, H=2, N=256, bs=128: 512 padded rows -> lse2 and delta 2048 bytes each,
+    # 2 x 2 x 2 transposed list entries and 4 counts, each rounded to 256 bytes
+    ws_mask = V.vsa_attn_bwd_workspace_bytes(1, 2, 256, 128, 0)
+    ws_list = V.vsa_attn_bwd_workspace_bytes(1, 2, 256, 128, 1)
+    assert ws_mask == 2048 + 2048 + 256 + 256
+    assert ws_list == ws_mask + 256                       # the mask built from the lists
+    assert V.vsa_attn_bwd_workspace_bytes(1, 2, 256, 32, 0) == 0
+    call = lambda **kw: L.vsa_block_sparse_attn_bwd(
+        kw.get("q", fake), fake, fake, fake, fake, kw.get("lse", fake), kw.get("dq", fake), fake, fake,
+        kw.get("B", 1), 2, 256, kw.get("D", 128), kw.get("dtype", 0), kw.get("bs", 128), None,
+        ctypes.byref(kw.get("blocks", blk)), kw.get("scale", 0.1), kw.get("ws", fake), kw.get("ws_bytes", ws_mask),
+        None)
+    assert call(q=None) == V.VSA_ERR_INVALID
+    assert call(lse=None) == V.VSA_ERR_INVALID
+    assert call(dq=ctypes.c_void_p(0x1008)) == V.VSA_ERR_INVALID
+    assert call(B=0) == V.VSA_ERR_INVALID
+    assert call(D=64) == V.VSA_ERR_UNSUPPORTED
+    assert call(dtype=1) == V.VSA_ERR_UNSUPPORTED
+    assert call(bs=32) == V.VSA_ERR_UNSUPPORTED
+    assert call(scale=float("nan")) == V.VSA_ERR_INVALID
+    assert call(blocks=V.vsa_blocks()) == V.VSA_ERR_INVALID
+    assert call(blocks=V.vsa_blocks(None, 0x1000, 0x1000, 0)) == V.VSA_ERR_INVALID
+    assert call(ws=None) == V.VSA_ERR_WORKSPACE
+    assert call(ws_bytes=ws_mask - 1) == V.VSA_ERR_WORKSPACE
+    assert str(ws_mask) in V.vsa_last_error()
+    # the list form needs the larger workspace
+    assert call(blocks=V.vsa_blocks(None, 0x1000, 0x1000, 2)) == V.VSA_ERR_WORKSPACE

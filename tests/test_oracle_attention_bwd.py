@@ -117,3 +117,23 @@ def test_bwd_softmax_invariants_and_padding():
 def test_bwd_flop_count():
     mask = np.ones((1, 1, 2, 2), np.uint8)
     assert OB.kept_flops_bwd(mask, 4, 8, 16) == 10 * 16 * 64
+
+
+def test_bwd_rows_matches_autograd_at_selected_positions():
+    """The sampled form (used at full video sizes) against torch autograd of the
+    dense masked softmax, with padding (blk_len) and a key block nobody keeps."""
+    H, N, D, bs = 2, 45, 8, 8
+    nb = -(-N // bs)
+    q, k, v, do = (rand((1, H, N, D), 110 + i) for i in range(4))
+    mask = (np.random.default_rng(11).random((H, nb, nb)) < 0.45).astype(np.uint8)
+    mask[:, :, 3] = 0
+    blk_len = np.array([8, 6, 8, 8, 2, 5])
+    valid = OA.block_valid(N, bs, blk_len)
+    q_rows = np.array([0, 7, 9, 14, 20, 33, 44])
+    k_rows = np.array([1, 8, 13, 25, 30, 34, 40, 44])
+    dq, dk, dv = OB.block_sparse_attention_bwd_rows(q, k, v, do, mask[None], bs, q_rows, k_rows, blk_len=blk_len)
+    rq, rk, rv = autograd_ref(q[0], k[0], v[0], do[0], token_mask(mask, bs, N, valid), 1.0 / np.sqrt(D))
+    np.testing.assert_allclose(dq[0], rq[:, q_rows], atol=1e-11)
+    np.testing.assert_allclose(dk[0], rk[:, k_rows], atol=1e-11)
+    np.testing.assert_allclose(dv[0], rv[:, k_rows], atol=1e-11)
+    assert (dk[0][:, [3]] == 0).all() and (dv[0][:, [3]] == 0).all()      # key 25 sits in block 3
