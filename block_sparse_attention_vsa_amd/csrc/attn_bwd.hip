@@ -8,7 +8,7 @@
 //   Delta_i = <dO_i, O_i>,   dQ_i = scale sum_j dS_ij k_j,  dK_j = scale sum_i dS_ij q_i,
 // every sum over kept (query block, key block) tiles only.
 //
-// Launches (no atomics; every sum has a fixed order):
+// Launches (no floating-point atomics; every sum has a fixed order):
 //  1. prep: per row, Delta_i in fp32 and LSE_i * log2(e) (+inf for a row that
 //     keeps nothing or is not valid, so its P is 0), both padded to whole blocks.
 //  2. lists: the block mask (built from the lists for the list form), then for
@@ -17,11 +17,10 @@
 //     64-key sub-tile, S^T = K Q^T and dP^T = V dO^T on MFMA (Q and dO held in
 //     registers), P^T and dS^T in fp32 on the VALU, dQ^T += K^T dS^T through
 //     transposing LDS reads of the same K tile.
-//  4. dV: one workgroup per (b, h, key block), 32 keys per wave, K in registers:
-//     per kept query sub-tile, S = Q K^T, P from the staged LSE, dV^T += dO^T P.
-//  5. dK: likewise with V in registers too: S, P, dP = dO V^T, dS,
-//     dK^T += Q^T dS (transposing reads of the Q tile).
-// dV and dK are separate launches so that each keeps 2 waves per SIMD.
+//  4. dK and dV: one workgroup per (b, h, key block), two waves per 32 keys
+//     (one forms S and P and adds to dV, the other forms dP, takes P through
+//     LDS and adds to dK); consecutive key blocks go to one XCD, where they share
+//     most of their query tiles in its L2.
 #include <math.h>
 
 #include "mfma_tile.h"
@@ -92,28 +91,63 @@ __global__ __launch_bounds__(256) void bwd_fill_u8_kernel(uint8_t* p, int64_t n)
     if (i < n) p[i] = 0;
 }
 
+// One wave per (b h, query block) row of the lists.
 __global__ __launch_bounds__(256) void bwd_list_to_mask_kernel(BwdArgs a, uint8_t* mask) {
-    const int64_t row = (int64_t)blockIdx.x * 256 + threadIdx.x;     // (b h, qb)
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
     if (row >= (int64_t)a.BH * a.nb) return;
     const int cnt = min(a.kv_cnt[row], a.max_kv);
     const int32_t* idx = a.kv_idx + row * a.max_kv;
-    for (int c = 0; c < cnt; ++c) {
+    for (int c = lane; c < cnt; c += 64) {
         const int kb = idx[c];
         if ((unsigned)kb < (unsigned)a.nb) mask[row * a.nb + kb] = 1;
     }
 }
 
-__global__ __launch_bounds__(256) void bwd_transpose_kernel(BwdArgs a) {
-    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;       // (b h, kb)
-    if (t >= (int64_t)a.BH * a.nb) return;
-    const int64_t bh = t / a.nb;
-    const int kb = (int)(t - bh * a.nb);
+// Transpose of the block mask into ascending per-key-block lists. A workgroup
+// takes 64 key blocks (one per lane, so every mask row is read as one 64-byte
+// segment) of one (b, h); its 16 waves split the query blocks into 16 ranges,
+// count their kept entries, and write them at offsets from a prefix over ranges.
+constexpr int kTrWaves = 16;
+constexpr int kTrChunk = 8;
+__global__ __launch_bounds__(kTrWaves * 64) void bwd_transpose_kernel(BwdArgs a, int col_groups) {
+    __shared__ int part[kTrWaves][64];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int64_t bh = blockIdx.x / col_groups;
+    const int kb = (int)(blockIdx.x - bh * col_groups) * 64 + lane;
+    const bool col_ok = kb < a.nb;
+    const int R = (a.nb + kTrWaves - 1) / kTrWaves;
+    const int r0 = min(a.nb, w * R), r1 = min(a.nb, r0 + R);
     const uint8_t* m = a.mask + bh * a.nb * (int64_t)a.nb + kb;
-    int32_t* out = a.qt_idx + t * a.nb;
     int c = 0;
-    for (int qb = 0; qb < a.nb; ++qb)
-        if (m[(int64_t)qb * a.nb]) out[c++] = qb;
-    a.qt_cnt[t] = c;
+    if (col_ok)
+        for (int qb = r0; qb < r1; qb += kTrChunk) {
+            uint8_t x[kTrChunk];
+#pragma unroll
+            for (int u = 0; u < kTrChunk; ++u) x[u] = (qb + u < r1) ? m[(int64_t)(qb + u) * a.nb] : 0;
+#pragma unroll
+            for (int u = 0; u < kTrChunk; ++u) c += x[u] != 0;
+        }
+    part[w][lane] = c;
+    __syncthreads();
+    int off = 0, tot = 0;
+#pragma unroll
+    for (int u = 0; u < kTrWaves; ++u) {
+        const int x = part[u][lane];
+        off += (u < w) ? x : 0;
+        tot += x;
+    }
+    if (!col_ok) return;
+    int32_t* out = a.qt_idx + (bh * a.nb + kb) * (int64_t)a.nb + off;
+    for (int qb = r0; qb < r1; qb += kTrChunk) {
+        uint8_t x[kTrChunk];        // loaded before any store: the stores may alias nothing they read
+#pragma unroll
+        for (int u = 0; u < kTrChunk; ++u) x[u] = (qb + u < r1) ? m[(int64_t)(qb + u) * a.nb] : 0;
+#pragma unroll
+        for (int u = 0; u < kTrChunk; ++u)
+            if (x[u]) *out++ = qb + u;
+    }
+    if (w == 0) a.qt_cnt[bh * a.nb + kb] = tot;
 }
 
 // Stores a 128-channel accumulator row (channel 32 dt + acc_key(0, x, half) in
@@ -240,42 +274,46 @@ __global__ __launch_bounds__(BS * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
     if (q_row < a.N) store_row_bf16(a.dq + head_off + (int64_t)q_row * D, acc, a.scale, q_ok, half);
 }
 
-// ---- 4./5. dV and dK: one workgroup per (b, h, key block), 32 keys per wave ----
-// Per query sub-tile (KT queries of a query block keeping this key block):
-// S = Q K^T with the Q tile as row operand and K in registers, so each lane holds
-// one key and the accumulator rows are queries; P = exp2(S scale log2 e - lse2)
-// with the sub-tile's lse2 (and delta) staged in LDS.
-template <int BS, bool DK>
-__global__ __launch_bounds__(BS * 2) __attribute__((amdgpu_waves_per_eu(2))) void bwd_dkv_kernel(BwdArgs a) {
+// ---- 4. dK and dV: one workgroup per (b, h, key block) -------------------------
+// Each 32-key group of the block has two waves: the P wave holds K in registers
+// and, per kept query sub-tile, forms S = Q K^T (the Q tile as row operand, so a
+// lane holds one key and the accumulator rows are queries), P = exp2(S scale
+// log2 e - lse2), hands P (fp32) to its partner through LDS and adds dO^T P to
+// dV^T; the dS wave holds V, forms dP = dO V^T meanwhile, then takes P and adds
+// Q^T dS, dS = P (dP - Delta), to dK^T. Both tiles are read as row and as
+// transposed operand (both-ways swizzle). S is thus formed once per pair for dK
+// and dV, and each Q / dO tile is streamed into LDS once for both.
+template <int BS>
+__global__ __launch_bounds__(BS * 4) __attribute__((amdgpu_waves_per_eu(2))) void bwd_dkv_kernel(BwdArgs a) {
     constexpr int D = 128, KT = (BS == 128) ? 64 : 32, NST = KT / 32, SUBB = KT * D * 2;
-    constexpr int WAVES = BS / 32, SUB = BS / KT;
-    // dV: Q row operand (rows swizzle), dO transposed operand (tr swizzle).
-    // dK: Q row and transposed operand (both-ways swizzle), dO row operand.
-    constexpr int SQ = DK ? kSwzBoth : kSwzRows;
-    constexpr int SO = DK ? kSwzRows : kSwzTr;
+    constexpr int G = BS / 32, WAVES = 2 * G, SUB = BS / KT;
     __shared__ __attribute__((aligned(1024))) uint8_t q0[SUBB];
     __shared__ __attribute__((aligned(1024))) uint8_t o0[SUBB];
     __shared__ __attribute__((aligned(1024))) uint8_t q1[SUBB];
     __shared__ __attribute__((aligned(1024))) uint8_t o1[SUBB];
     __shared__ __attribute__((aligned(16))) float ld0[2 * KT];     // lse2 | delta of the sub-tile's queries
     __shared__ __attribute__((aligned(16))) float ld1[2 * KT];
+    __shared__ __attribute__((aligned(16))) float pex[G * NST * 1024];   // P, [group][st][x / 4][lane][4]
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int l32 = lane & 31, half = lane >> 5;
+    const int half = lane >> 5;
+    // waves w and w + G share a SIMD (waves are placed round-robin), so each
+    // SIMD carries one P wave and one dS wave of the same key group
+    const bool ds_wave = w >= G;
+    const int kg = ds_wave ? w - G : w;
     const int item = xcd_remap(blockIdx.x, a.BH * a.nb);
     const int bh = item / a.nb, kb = item - bh * a.nb;
     const int64_t head_off = (int64_t)bh * a.N * D;
     const int valid_k = bwd_block_valid(a.blk_len, kb, BS, a.N);
-    const bool wave_active = 32 * w < valid_k;
-    const int k_local = 32 * w + l32;
+    const bool active = 32 * kg < valid_k;
+    const int k_local = 32 * kg + (lane & 31);
     const int k_row = kb * BS + k_local;
     const bool k_ok = k_local < valid_k;
 
     const int cnt = ld_const(a.qt_cnt, item);
     const int32_t* list_g = a.qt_idx + (int64_t)item * a.nb;
-    const PairTileDma<WAVES, SQ, SO, KT> dma(lane, w);
-    const TileAddr<SQ> adq(lane);
-    const TileAddr<SO> ado(lane);
+    const PairTileDma<WAVES, kSwzBoth, kSwzBoth, KT> dma(lane, w);
+    const TileAddr<kSwzBoth> ad(lane);
     const int head_bytes = a.N * D * 2;
     const float* lse2_head = a.lse2 + (int64_t)bh * a.nb * BS;
     const float* delta_head = a.delta + (int64_t)bh * a.nb * BS;
@@ -287,52 +325,77 @@ __global__ __launch_bounds__(BS * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
         // lse2 and delta of the KT queries: 4 floats per lane, lanes [0, KT / 4) of wave 0
         if (w == 0 && lane < KT / 4) {
             dma16(lse2_head, ld_bytes, ldd, row0 * 4 + lane * 16, 0);
-            if constexpr (DK) dma16(delta_head, ld_bytes, ldd + KT, row0 * 4 + lane * 16, 0);
+            dma16(delta_head, ld_bytes, ldd + KT, row0 * 4 + lane * 16, 0);
         }
     };
 
-    bf16x8 kf[8], vf[8];
-    load_q_frag<D>(kf, a.k + head_off + (int64_t)k_row * D, k_ok, half);
-    if constexpr (DK) load_q_frag<D>(vf, a.v + head_off + (int64_t)k_row * D, k_ok, half);
+    bf16x8 kv[8];                                     // K (P wave) or V (dS wave)
+    load_q_frag<D>(kv, (ds_wave ? a.v : a.k) + head_off + (int64_t)k_row * D, k_ok, half);
+    f32x4* pg = reinterpret_cast<f32x4*>(pex) + kg * NST * 256;
 
-    f32x16 acc[4];
+    f32x16 acc[4];                                    // dV^T (P wave) or dK^T (dS wave)
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) acc[dt] = f32x16{};
 
     auto compute = [&](const uint8_t* qt, const uint8_t* ot, const float* ldt) __attribute__((always_inline)) {
-        if (!wave_active) return;
-        // one 32-query half at a time keeps the live scores within the register budget
+        bf16x8 pf[NST][2];
+        f32x16 dp[NST];
+        // phase 1: S and P (P wave) | dP (dS wave)
+        if (active) {
+            if (!ds_wave) {
 #pragma unroll
-        for (int st = 0; st < NST; ++st) {
-            const f32x16 s = tile_rows_mma_at(qt, st, kf, adq);                  // S = Q K^T: lane = key
-            f32x16 dp = f32x16{};
-            if constexpr (DK) dp = tile_rows_mma_at(ot, st, vf, ado);            // dP = dO V^T
-            bf16x8 pf[2];
+                for (int st = 0; st < NST; ++st) {
+                    const f32x16 s = tile_rows_mma_at(qt, st, kv, ad);          // S = Q K^T: lane = key
 #pragma unroll
-            for (int xg = 0; xg < 4; ++xg) {
-                // queries 32 st + 8 xg + 4 half + [0, 4) of the sub-tile
-                const int q0i = 32 * st + 8 * xg + 4 * half;
-                const f32x4 l4 = *reinterpret_cast<const f32x4*>(ldt + q0i);
-                f32x4 d4 = f32x4{};
-                if constexpr (DK) d4 = *reinterpret_cast<const f32x4*>(ldt + KT + q0i);
+                    for (int xg = 0; xg < 4; ++xg) {
+                        // queries 32 st + 8 xg + 4 half + [0, 4) of the sub-tile
+                        const f32x4 l4 = *reinterpret_cast<const f32x4*>(ldt + 32 * st + 8 * xg + 4 * half);
+                        f32x4 p4;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int x = 4 * xg + e;
-                    float p = __builtin_amdgcn_exp2f(fmaf(s[x], a.scale_log2, -l4[e]));
-                    if (!k_ok) p = 0.f;
-                    const float val = DK ? p * (dp[x] - d4[e]) : p;
-                    pf[x >> 3][x & 7] = (__bf16)val;
+                        for (int e = 0; e < 4; ++e) {
+                            float p = __builtin_amdgcn_exp2f(fmaf(s[4 * xg + e], a.scale_log2, -l4[e]));
+                            p4[e] = k_ok ? p : 0.f;
+                            pf[st][xg >> 1][4 * (xg & 1) + e] = (__bf16)p4[e];
+                        }
+                        pg[(st * 4 + xg) * 64 + lane] = p4;
+                    }
                 }
+            } else {
+#pragma unroll
+                for (int st = 0; st < NST; ++st) dp[st] = tile_rows_mma_at(ot, st, kv, ad);   // dP = dO V^T
             }
+        }
+        __syncthreads();                              // P visible to the dS waves
+        // phase 2: dV^T += dO^T P (P wave) | dS, dK^T += Q^T dS (dS wave)
+        if (!active) return;
+        if (!ds_wave) {
 #pragma unroll
-            for (int dt = 0; dt < 4; ++dt)
+            for (int st = 0; st < NST; ++st)
 #pragma unroll
-                for (int g = 0; g < 2; ++g) {
-                    bf16x8 a_op;
-                    if constexpr (DK) a_op = tile_tr_operand_at(qt, dt, st, g, adq);       // Q^T
-                    else a_op = tile_tr_operand_at(ot, dt, st, g, ado);                    // dO^T
-                    acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_op, pf[g], acc[dt], 0, 0, 0);
+                for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+                    for (int g = 0; g < 2; ++g)
+                        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tile_tr_operand_at(ot, dt, st, g, ad),
+                                                                          pf[st][g], acc[dt], 0, 0, 0);
+        } else {
+#pragma unroll
+            for (int st = 0; st < NST; ++st) {
+                bf16x8 dsf[2];
+#pragma unroll
+                for (int xg = 0; xg < 4; ++xg) {
+                    const f32x4 d4 = *reinterpret_cast<const f32x4*>(ldt + KT + 32 * st + 8 * xg + 4 * half);
+                    const f32x4 p4 = pg[(st * 4 + xg) * 64 + lane];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        dsf[xg >> 1][4 * (xg & 1) + e] = (__bf16)(p4[e] * (dp[st][4 * xg + e] - d4[e]));
                 }
+#pragma unroll
+                for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+                    for (int g = 0; g < 2; ++g)
+                        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tile_tr_operand_at(qt, dt, st, g, ad),
+                                                                          dsf[g], acc[dt], 0, 0, 0);
+            }
         }
     };
 
@@ -340,7 +403,7 @@ __global__ __launch_bounds__(BS * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
     if (n_sub > 0) issue(0, q0, o0, ld0);
     for (int i = 0; i < n_sub; i += 2) {
         __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
+        __syncthreads();                              // stage ready; the previous sub-tile's P consumed
         if (i + 1 < n_sub) issue(i + 1, q1, o1, ld1);
         compute(q0, o0, ld0);
         if (i + 1 < n_sub) {
@@ -351,8 +414,8 @@ __global__ __launch_bounds__(BS * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
         }
     }
     if (k_row < a.N) {
-        uint16_t* dst = (DK ? a.dk : a.dv) + head_off + (int64_t)k_row * D;
-        store_row_bf16(dst, acc, DK ? a.scale : 1.f, k_ok, half);
+        uint16_t* dst = (ds_wave ? a.dk : a.dv) + head_off + (int64_t)k_row * D;
+        store_row_bf16(dst, acc, ds_wave ? a.scale : 1.f, k_ok, half);
     }
 }
 
@@ -443,12 +506,14 @@ extern "C" int vsa_block_sparse_attn_bwd(const void* q, const void* k, const voi
         uint8_t* m = ws + pl.off_mask;
         const int64_t n = BH * nb * nb;
         hipLaunchKernelGGL(bwd_fill_u8_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, m, n);
-        hipLaunchKernelGGL(bwd_list_to_mask_kernel, dim3((unsigned)((BH * nb + 255) / 256)), dim3(256), 0, s, a, m);
+        hipLaunchKernelGGL(bwd_list_to_mask_kernel, dim3((unsigned)((BH * nb + 3) / 4)), dim3(256), 0, s, a, m);
         a.mask = m;
     } else {
         a.mask = blocks->mask;
     }
-    hipLaunchKernelGGL(bwd_transpose_kernel, dim3((unsigned)((BH * nb + 255) / 256)), dim3(256), 0, s, a);
+    const int col_groups = (int)((nb + 63) / 64);
+    hipLaunchKernelGGL(bwd_transpose_kernel, dim3((unsigned)(BH * col_groups)), dim3(kTrWaves * 64), 0, s, a,
+                       col_groups);
     st = launch_status("vsa_block_sparse_attn_bwd (lists)");
     if (st) return st;
     // dQ walks the caller's rows (list, or the mask through compaction)
@@ -458,12 +523,10 @@ extern "C" int vsa_block_sparse_attn_bwd(const void* q, const void* k, const voi
     const size_t shm = has_list ? 0 : (((size_t)nb * 2 + 15) & ~(size_t)15);
     if (bs == 128) {
         hipLaunchKernelGGL((bwd_dq_kernel<128>), grid, dim3(256), shm, s, aq);
-        hipLaunchKernelGGL((bwd_dkv_kernel<128, false>), grid, dim3(256), 0, s, a);
-        hipLaunchKernelGGL((bwd_dkv_kernel<128, true>), grid, dim3(256), 0, s, a);
+        hipLaunchKernelGGL((bwd_dkv_kernel<128>), grid, dim3(512), 0, s, a);
     } else {
         hipLaunchKernelGGL((bwd_dq_kernel<64>), grid, dim3(128), shm, s, aq);
-        hipLaunchKernelGGL((bwd_dkv_kernel<64, false>), grid, dim3(128), 0, s, a);
-        hipLaunchKernelGGL((bwd_dkv_kernel<64, true>), grid, dim3(128), 0, s, a);
+        hipLaunchKernelGGL((bwd_dkv_kernel<64>), grid, dim3(256), 0, s, a);
     }
     return launch_status(fn);
 }
