@@ -369,6 +369,32 @@ def main():
     print(json.dumps(out), flush=True)
 
 
+def time_backward(torch, V, T, q, k, v, bs, fwd_flops, reps=4, **blocks):
+    """Forward (with LSE) once, then the backward under the same block set, timed
+    over reps - 1 calls after one untimed call; dO is seeded unit normal."""
+    g = torch.Generator(device=q.device).manual_seed(7)
+    do = torch.randn(q.shape, generator=g, device=q.device, dtype=torch.float32).to(q.dtype)
+    o, lse = V.vsa_block_sparse_attn_fwd(q, k, v, bs, return_lse=True, **blocks)
+    B, H, N, _ = q.shape
+    ws = torch.empty((V.vsa_attn_bwd_workspace_bytes(B, H, N, bs, "kv_idx" in blocks),), dtype=torch.uint8,
+                     device=q.device)
+    grads = [torch.empty_like(q) for _ in range(3)]
+    ms = []
+    for rep in range(reps):
+        e0 = T.ev()
+        V.vsa_block_sparse_attn_bwd(q, k, v, o, lse, do, bs, dq=grads[0], dk=grads[1], dv=grads[2], workspace=ws,
+                                    **blocks)
+        e1 = T.ev()
+        torch.cuda.synchronize()
+        if rep:
+            ms.append(e0.elapsed_time(e1))
+    t = float(np.mean(ms))
+    fl = 2.5 * fwd_flops          # 10 D per kept pair (S, dP, dV, dQ, dK) against the forward's 4 D
+    del do, o, lse, ws, grads
+    return {"ms": round(t, 4), "flops": fl, "tflops": round(fl / (t * 1e-3) / 1e12, 2),
+            "pct_mfma_peak": round(100 * fl / (t * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2)}
+
+
 def extra_layers(torch, V, PL, T):
     """Cube top-p/top-k layer (Wan shape) and long-horizon layer, each timed over a
     few runs with per-call events: the pooling/score and selection steps live here."""
@@ -411,7 +437,19 @@ def extra_layers(torch, V, PL, T):
                                    "separate_total_ms": round(ms["separate_permute_qkv"] + ms["separate_attention"]
                                                               + ms["separate_permute_o"], 4),
                                    "bit_identical": bool(torch.equal(o_f, o_s))}
-    del q, k, v, qm, km, vm, om, o_f, o_s, cand
+    del qm, km, vm, om, o_f, o_s, cand
+    torch.cuda.empty_cache()
+
+    # backward (dQ, dK, dV) at the same shape with the spatial w=1 block mask on
+    # every head, natural order (trainable sparse attention)
+    m = V.vsa_pattern_mask(w.grid, w.bs, V.VSA_PATTERN_SPATIAL, w.extra["w_spatial"])
+    mask = m.reshape(1, 1, w.nb, w.nb).expand(1, w.H, w.nb, w.nb).contiguous()
+    bi, bc = V.vsa_mask_to_list(mask)
+    res["attn_bwd_spatial_wan480"] = time_backward(torch, V, T, q, k, v, w.bs,
+                                                   kept_flops_from_lists(bi, bc, w.N, w.bs, 128), mask=mask)
+    res["attn_bwd_spatial_wan480"]["what"] = ("vsa_block_sparse_attn_bwd, [1,12,32760,128] bf16, bs 128, spatial "
+                                              "w=1 block mask on all heads")
+    del q, k, v, m, mask, bi, bc
     torch.cuda.empty_cache()
 
     w = WAN480_CUBE
@@ -442,7 +480,9 @@ def extra_layers(torch, V, PL, T):
     t_att = float(np.mean(times["a7_attention"]))
     res["cube_topp_wan480"] = {"ms": {k_: round(float(np.mean(v_)), 4) for k_, v_ in times.items()},
                                "k_max": k_max, "mean_kept": round(float(cnt.float().mean().item()), 2),
-                               "attn_tflops": round(fl / (t_att * 1e-3) / 1e12, 2)}
+                               "attn_tflops": round(fl / (t_att * 1e-3) / 1e12, 2),
+                               "backward": time_backward(torch, V, T, qc, kc, vc, 64, fl, kv_idx=idx, kv_cnt=cnt,
+                                                         blk_len=blk)}
     del q, k, v, qc, kc, vc, oc, o, S
     torch.cuda.empty_cache()
 
