@@ -64,6 +64,15 @@ _SIGNATURES = {
     "vsa_attn_bwd_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I]),
     "vsa_block_sparse_attn_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P,
                                        ctypes.POINTER(vsa_blocks), _F, _P, _SZ, _P]),
+    "vsa_kmeans_workspace_bytes": (_SZ, [_I, _I, _I, _I]),
+    "vsa_kmeans": (_I, [_P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _SZ, _P]),
+    "vsa_cluster_order_workspace_bytes": (_SZ, [_I, _I, _I, _I]),
+    "vsa_cluster_order": (_I, [_P, _P, _I, _I, _I, _I, _P, _P, _P, _SZ, _P]),
+    "vsa_gather_rows": (_I, [_P, _P, _I, _I, _I, _I, _I, _P, _I, _P]),
+    "vsa_cluster_scores": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _F, _P, _P]),
+    "vsa_varlen_attn_workspace_bytes": (_SZ, [_I, _I, _I]),
+    "vsa_varlen_sparse_attn_fwd": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _I, _P, _I,
+                                        ctypes.POINTER(vsa_blocks), _F, _P, _SZ, _P]),
     "vsa_check_block_list_host": (_I, [_P, _P, _I64, _I, _I]),
 }
 
@@ -451,6 +460,110 @@ def vsa_block_sparse_attn_bwd(q, k, v, o, lse, dout, bs: int, mask=None, kv_idx=
                                            0 if workspace is None else workspace.numel(), _stream(q.device)),
            "vsa_block_sparse_attn_bwd")
     return dq, dk, dv
+
+
+def vsa_kmeans_workspace_bytes(B, H, C, D) -> int:
+    return lib().vsa_kmeans_workspace_bytes(B, H, C, D)
+
+
+def vsa_kmeans(x, C: int, iters: int, out=None, workspace=None):
+    """Lloyd's k-means of every (b, h) of x [B, H, N, D] (bf16): returns
+    (centroids fp32 [B, H, C, D], labels int32 [B, H, N], counts int32 [B, H, C])."""
+    torch = _torch()
+    _need(x, "x", ndim=4)
+    B, H, N, D = x.shape
+    if out is None:
+        out = (torch.empty((B, H, C, D), dtype=torch.float32, device=x.device),
+               torch.empty((B, H, N), dtype=torch.int32, device=x.device),
+               torch.empty((B, H, C), dtype=torch.int32, device=x.device))
+    cent, lab, cnt = out
+    if workspace is None:
+        workspace = torch.empty((max(1, vsa_kmeans_workspace_bytes(B, H, C, D)),), dtype=torch.uint8,
+                                device=x.device)
+    _check(lib().vsa_kmeans(_ptr(x), B, H, N, D, _dtype_code(x), C, iters, _ptr(cent), _ptr(lab), _ptr(cnt),
+                            _ptr(workspace), workspace.numel(), _stream(x.device)), "vsa_kmeans")
+    return cent, lab, cnt
+
+
+def vsa_cluster_order_workspace_bytes(B, H, N, C) -> int:
+    return lib().vsa_cluster_order_workspace_bytes(B, H, N, C)
+
+
+def vsa_cluster_order(labels, counts, out=None, workspace=None):
+    """Stable cluster-major order: (perm int32 [B, H, N], offsets int32 [B, H, C + 1])."""
+    torch = _torch()
+    _need(labels, "labels", torch.int32, 3)
+    _need(counts, "counts", torch.int32, 3)
+    B, H, N = labels.shape
+    C = counts.shape[-1]
+    if out is None:
+        out = (torch.empty((B, H, N), dtype=torch.int32, device=labels.device),
+               torch.empty((B, H, C + 1), dtype=torch.int32, device=labels.device))
+    perm, off = out
+    if workspace is None:
+        workspace = torch.empty((max(1, vsa_cluster_order_workspace_bytes(B, H, N, C)),), dtype=torch.uint8,
+                                device=labels.device)
+    _check(lib().vsa_cluster_order(_ptr(labels), _ptr(counts), B, H, N, C, _ptr(perm), _ptr(off), _ptr(workspace),
+                                   workspace.numel(), _stream(labels.device)), "vsa_cluster_order")
+    return perm, off
+
+
+def vsa_gather_rows(src, perm, inverse: bool = False, out=None):
+    torch = _torch()
+    _need(src, "src", ndim=4)
+    _need(perm, "perm", torch.int32, 3)
+    B, H, N, D = src.shape
+    if out is None:
+        out = torch.empty_like(src)
+    _check(lib().vsa_gather_rows(_ptr(src), _ptr(out), B, H, N, D, _dtype_code(src), _ptr(perm), int(bool(inverse)),
+                                 _stream(src.device)), "vsa_gather_rows")
+    return out
+
+
+def vsa_cluster_scores(cq, ck, k_counts, scale=None, out=None):
+    torch = _torch()
+    _need(cq, "cq", torch.float32, 4)
+    _need(ck, "ck", torch.float32, 4)
+    _need(k_counts, "k_counts", torch.int32, 3)
+    B, H, Cq, D = cq.shape
+    Ck = ck.shape[2]
+    scale = default_scale(D) if scale is None else scale
+    if out is None:
+        out = torch.empty((B, H, Cq, Ck), dtype=torch.float32, device=cq.device)
+    _check(lib().vsa_cluster_scores(_ptr(cq), _ptr(ck), _ptr(k_counts), B, H, Cq, Ck, D, scale, _ptr(out),
+                                    _stream(cq.device)), "vsa_cluster_scores")
+    return out
+
+
+def vsa_varlen_attn_workspace_bytes(B, H, Cq) -> int:
+    return lib().vsa_varlen_attn_workspace_bytes(B, H, Cq)
+
+
+def vsa_varlen_sparse_attn_fwd(q, k, v, q_off, k_off, mask=None, kv_idx=None, kv_cnt=None, scale=None,
+                               return_lse=False, out=None, lse=None, workspace=None):
+    """Attention over clusters in cluster-major storage (q by query cluster, k / v
+    by key cluster; q_off [B, H, Cq + 1], k_off [B, H, Ck + 1])."""
+    torch = _torch()
+    _need(q, "q", ndim=4)
+    _need(k, "k", q.dtype, 4)
+    _need(v, "v", q.dtype, 4)
+    _need(q_off, "q_off", torch.int32, 3)
+    _need(k_off, "k_off", torch.int32, 3)
+    B, H, N, D = q.shape
+    Cq, Ck = q_off.shape[-1] - 1, k_off.shape[-1] - 1
+    scale = default_scale(D) if scale is None else scale
+    if out is None:
+        out = torch.empty_like(q)
+    if return_lse and lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    blocks = _blocks_arg(q, 0, mask, kv_idx, kv_cnt)
+    if workspace is None:
+        workspace = torch.empty((vsa_varlen_attn_workspace_bytes(B, H, Cq),), dtype=torch.uint8, device=q.device)
+    _check(lib().vsa_varlen_sparse_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, N, D,
+                                            _dtype_code(q), _ptr(q_off), Cq, _ptr(k_off), Ck, ctypes.byref(blocks),
+                                            scale, _ptr(workspace), workspace.numel(), _stream(q.device)),
+           "vsa_varlen_sparse_attn_fwd")
+    return (out, lse) if return_lse else out
 
 
 def vsa_check_block_list_host(kv_idx: np.ndarray, kv_cnt: np.ndarray, nkb: int) -> None:

@@ -1,0 +1,348 @@
+// Attention over variable-size clusters in cluster-major storage, on gfx950.
+//
+// Sparse VideoGen2 page, Abstract: after the semantic-aware permutation the
+// critical tokens are dense, so the kernel computes them without padding. Q is
+// stored cluster-major by query cluster (cluster a in rows [q_off[a], q_off[a+1])),
+// K and V by key cluster (k_off); every query of cluster a attends to the keys
+// of the key clusters kept for a:
+//   O_i = sum_{j in kept clusters of a} softmax_j(scale <q_i, k_j>) v_j.
+//
+// One workgroup per (b, h, query cluster, chunk of at most 128 rows), 4 waves of
+// 32 rows, Q in registers. The kept key clusters are laid end to end into one
+// packed key sequence, walked in 64-key sub-tiles: every DMA lane maps its
+// packed position to a row of K / V (a per-workgroup LDS table holds each kept
+// cluster's packed start and row start, and each sub-tile's first cluster), so
+// clusters of any size share sub-tiles and only the last sub-tile of a
+// workgroup is partial. The score / softmax / P V core is the one of the block
+// kernel (S^T = K Q^T on v_mfma_f32_32x32x16_bf16, online softmax in the log2
+// domain with a lazily moved offset, V^T through transposing LDS reads).
+#include <math.h>
+
+#include "mfma_tile.h"
+
+namespace vsa {
+
+constexpr int kVarBS = 128;          // query rows per workgroup
+constexpr int kVarKT = 64;           // keys per sub-tile
+constexpr int kVarMaxMask = 4096;    // key clusters per mask row (mask form)
+
+struct VarArgs {
+    const uint16_t* q;
+    const uint16_t* k;
+    const uint16_t* v;
+    uint16_t* o;
+    float* lse;
+    const int32_t* q_off;          // [BH, Cq + 1]
+    const int32_t* k_off;          // [BH, Ck + 1]
+    const uint8_t* mask;           // [BH, Cq, Ck] or null
+    const int32_t* kv_idx;         // [BH, Cq, max_kv] or null
+    const int32_t* kv_cnt;         // [BH, Cq]
+    int32_t max_kv;
+    const int32_t* chunk_start;    // [BH, Cq + 1]: first chunk of each query cluster
+    int32_t N, Cq, Ck, BH, max_chunks, max_entries, max_subs;
+    float scale_log2;
+};
+
+// chunks of 128 rows per query cluster, as an exclusive scan: one wave per (b, h)
+__global__ __launch_bounds__(64) void varlen_chunks_kernel(VarArgs a, int32_t* chunk_start) {
+    const int64_t bh = blockIdx.x;
+    const int lane = threadIdx.x;
+    const int32_t* off = a.q_off + bh * (a.Cq + 1);
+    int32_t* out = chunk_start + bh * (a.Cq + 1);
+    int run = 0;
+    for (int c0 = 0; c0 < a.Cq; c0 += 64) {
+        const int c = c0 + lane;
+        int v = 0;
+        if (c < a.Cq) {
+            const int n = off[c + 1] - off[c];
+            v = n > 0 ? (n + kVarBS - 1) / kVarBS : 0;
+        }
+        int x = v;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int y = __shfl_up(x, d);
+            if (lane >= d) x += y;
+        }
+        if (c < a.Cq) out[c] = run + x - v;
+        run += __shfl(x, 63);
+    }
+    if (lane == 0) out[a.Cq] = run;
+}
+
+// Exclusive scan of one value per thread over a 256-thread workgroup; returns
+// the prefix and sets `total` (all threads). `tmp` holds 4 ints.
+__device__ __forceinline__ int block_scan_256(int v, int* tmp, int& total) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    int x = v;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int y = __shfl_up(x, d);
+        if (lane >= d) x += y;
+    }
+    if (lane == 63) tmp[w] = x;
+    __syncthreads();
+    int before = 0;
+    total = 0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int t = tmp[u];
+        before += (u < w) ? t : 0;
+        total += t;
+    }
+    __syncthreads();
+    return before + x - v;
+}
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void attn_varlen_kernel(VarArgs a) {
+    constexpr int D = 128, KT = kVarKT, NST = KT / 32, SUBB = KT * D * 2, WAVES = 4, THREADS = 256;
+    constexpr float TAU = 8.f;
+    __shared__ __attribute__((aligned(1024))) uint8_t k0[SUBB];
+    __shared__ __attribute__((aligned(1024))) uint8_t v0[SUBB];
+    __shared__ __attribute__((aligned(1024))) uint8_t k1[SUBB];
+    __shared__ __attribute__((aligned(1024))) uint8_t v1[SUBB];
+    __shared__ int scan_tmp[4];
+    __shared__ int wave_cnt[WAVES];
+    // dynamic: pp[max_entries + 1] | kst[max_entries] | t0[max_subs] | list16[Ck] (mask form)
+    extern __shared__ __attribute__((aligned(16))) int32_t dyn[];
+    int32_t* pp = dyn;
+    int32_t* kst = pp + a.max_entries + 1;
+    int32_t* t0 = kst + a.max_entries;
+    int16_t* list16 = reinterpret_cast<int16_t*>(t0 + a.max_subs);
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int l32 = lane & 31, half = lane >> 5;
+    const int item = xcd_remap(blockIdx.x, a.BH * a.max_chunks);
+    const int bh = item / a.max_chunks, ci = item - bh * a.max_chunks;
+    const int32_t* cs = a.chunk_start + (int64_t)bh * (a.Cq + 1);
+    if (ci >= ld_const(cs, a.Cq)) return;                      // past this head's chunks (uniform)
+    int lo = 0, hi = a.Cq;                                      // cs[lo] <= ci < cs[hi]
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (ld_const(cs, mid) <= ci) lo = mid;
+        else hi = mid;
+    }
+    const int qa = lo;
+    const int32_t* qo = a.q_off + (int64_t)bh * (a.Cq + 1);
+    const int q0 = ld_const(qo, qa) + (ci - ld_const(cs, qa)) * kVarBS;
+    // rows outside [0, N) (malformed offsets) are never read or written
+    const int valid_q = q0 < 0 ? 0 : max(0, min(kVarBS, min(ld_const(qo, qa + 1), a.N) - q0));
+    const bool wave_active = 32 * w < valid_q;
+    const int64_t head_off = (int64_t)bh * a.N * D;
+    const int64_t row_item = (int64_t)bh * a.Cq + qa;
+
+    // ---- kept key clusters and the packed-sequence table --------------------------
+    int cnt;
+    const int32_t* list_g = nullptr;
+    if (a.mask) {
+        cnt = compact_mask_row<THREADS>(a.mask + row_item * a.Ck, a.Ck, list16, wave_cnt);
+    } else {
+        cnt = min(ld_const(a.kv_cnt, row_item), a.max_kv);
+        list_g = a.kv_idx + row_item * a.max_kv;
+    }
+    const int32_t* ko = a.k_off + (int64_t)bh * (a.Ck + 1);
+    int L = 0;
+    for (int e0 = 0; e0 < cnt; e0 += THREADS) {
+        const int e = e0 + tid;
+        int len = 0, start = 0;
+        if (e < cnt) {
+            const int c = list_g ? list_g[e] : (int)list16[e];
+            if ((unsigned)c < (unsigned)a.Ck) {
+                start = ko[c];
+                len = ko[c + 1] - start;
+            }
+        }
+        int tot;
+        const int pos = L + block_scan_256(len, scan_tmp, tot);
+        if (e < cnt) {
+            pp[e] = pos;
+            kst[e] = start;
+        }
+        L += tot;
+    }
+    L = min(L, a.max_subs * KT);          // repeated clusters cannot overrun the table
+    if (tid == 0) pp[cnt] = L;
+    __syncthreads();
+    for (int e = tid; e < cnt; e += THREADS) {
+        const int p0 = pp[e], p1 = min(pp[e + 1], L);
+        for (int i = (p0 + KT - 1) / KT; i * KT < p1; ++i) t0[i] = e;
+    }
+    __syncthreads();
+    const int n_sub = (L + KT - 1) / KT;
+
+    const SubTileDma<WAVES, kVSwz4, KT> dma(lane, w);
+    const int head_bytes = a.N * D * 2;
+    auto issue = [&](int i, uint8_t* kd, uint8_t* vd) {
+        int e = t0[i];
+#pragma unroll
+        for (int u = 0; u < SubTileDma<WAVES, kVSwz4, KT>::IPW; ++u) {
+            const int ins = w + WAVES * u;
+            const int p = i * KT + 4 * ins + (lane >> 4);
+            int row = a.N;                                      // past the head: reads zeros
+            if (p < L) {
+                while (e + 1 < cnt && pp[e + 1] <= p) ++e;
+                row = kst[e] + (p - pp[e]);
+            }
+            dma16(a.k + head_off, head_bytes, kd + ins * 1024, row * 256 + dma.ck[u % SubTileDma<WAVES, kVSwz4, KT>::NCLS], 0);
+            dma16(a.v + head_off, head_bytes, vd + ins * 1024, row * 256 + dma.cv, 0);
+        }
+    };
+
+    const int q_local = 32 * w + l32;
+    const int q_row = q0 + q_local;
+    const bool q_ok = q_local < valid_q;
+    bf16x8 qf[D / 16];
+    load_q_frag<D>(qf, a.q + head_off + (int64_t)q_row * D, q_ok, half);
+
+    f32x16 o_acc[D / 32];
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) o_acc[dt] = f32x16{};
+    float m_run = -INFINITY, l_run = 0.f;
+
+    auto compute = [&](int i, const uint8_t* kt, const uint8_t* vt) __attribute__((always_inline)) {
+        const int vs = min(KT, L - i * KT);
+        if (!wave_active) return;
+        f32x16 s[NST];
+        sub_scores<NST>(s, kt, qf, l32, half);
+        if (vs < KT) {
+#pragma unroll
+            for (int st = 0; st < NST; ++st)
+#pragma unroll
+                for (int x = 0; x < 16; ++x)
+                    if (acc_key(st, x, half) >= vs) s[st][x] = -INFINITY;
+        }
+        float mx = -INFINITY;
+#pragma unroll
+        for (int st = 0; st < NST; ++st)
+#pragma unroll
+            for (int x = 0; x < 16; ++x) mx = fmaxf(mx, s[st][x]);
+        mx = pair_max(mx);
+        const float m_tile = mx * a.scale_log2;
+        const bool upd = m_tile > m_run + TAU;
+        const float m_new = upd ? m_tile : m_run;
+        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+        if (__ballot(upd)) {
+            const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+            l_run *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+                for (int x = 0; x < 16; ++x) o_acc[dt][x] *= alpha;
+        }
+        m_run = m_new;
+        bf16x8 pf[NST][2];
+        float ps[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int st = 0; st < NST; ++st)
+#pragma unroll
+            for (int x = 0; x < 16; ++x) {
+                const float p = __builtin_amdgcn_exp2f(fmaf(s[st][x], a.scale_log2, -m_use));
+                ps[x & 3] += p;
+                pf[st][x >> 3][x & 7] = (__bf16)p;
+            }
+        l_run += (ps[0] + ps[1]) + (ps[2] + ps[3]);
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+            for (int st = 0; st < NST; ++st)
+#pragma unroll
+                for (int g = 0; g < 2; ++g)
+                    o_acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sub_vt_operand(vt, dt, st, g, lane),
+                                                                        pf[st][g], o_acc[dt], 0, 0, 0);
+    };
+
+    if (n_sub > 0) issue(0, k0, v0);
+    for (int i = 0; i < n_sub; i += 2) {
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (i + 1 < n_sub) issue(i + 1, k1, v1);
+        compute(i, k0, v0);
+        if (i + 1 < n_sub) {
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+            if (i + 2 < n_sub) issue(i + 2, k0, v0);
+            compute(i + 1, k1, v1);
+        }
+    }
+
+    const float l_tot = pair_sum(l_run);
+    if (q_ok) {
+        const bool has = l_tot > 0.f;
+        const float inv = has ? 1.f / l_tot : 0.f;
+        uint16_t* orow = a.o + head_off + (int64_t)q_row * D;
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                const __bf16 b0 = (__bf16)(o_acc[dt][4 * jj + 0] * inv);
+                const __bf16 b1 = (__bf16)(o_acc[dt][4 * jj + 1] * inv);
+                const __bf16 b2 = (__bf16)(o_acc[dt][4 * jj + 2] * inv);
+                const __bf16 b3 = (__bf16)(o_acc[dt][4 * jj + 3] * inv);
+                u32x2 pk;
+                pk.x = (uint32_t)__builtin_bit_cast(uint16_t, b0) | ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16);
+                pk.y = (uint32_t)__builtin_bit_cast(uint16_t, b2) | ((uint32_t)__builtin_bit_cast(uint16_t, b3) << 16);
+                *reinterpret_cast<u32x2*>(orow + 32 * dt + 8 * jj + 4 * half) = pk;
+            }
+        if (a.lse && half == 0)
+            a.lse[(int64_t)bh * a.N + q_row] = has ? (m_run + log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
+    }
+}
+
+}  // namespace vsa
+
+using namespace vsa;
+
+extern "C" size_t vsa_varlen_attn_workspace_bytes(int B, int H, int Cq) {
+    if (B <= 0 || H <= 0 || Cq <= 0) return 0;
+    return (size_t)B * H * (Cq + 1) * 4;
+}
+
+extern "C" int vsa_varlen_sparse_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                                          int H, int N, int D, int dtype, const int32_t* q_off, int Cq,
+                                          const int32_t* k_off, int Ck, const vsa_blocks* blocks, float scale,
+                                          void* workspace, size_t ws_bytes, void* stream) {
+    const char* fn = "vsa_varlen_sparse_attn_fwd";
+    if (!q || !k || !v || !o || !q_off || !k_off) return fail(VSA_ERR_INVALID, "%s: null tensor", fn);
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+        return fail(VSA_ERR_INVALID, "%s: tensors must be 16-byte aligned", fn);
+    if (B <= 0 || H <= 0 || N <= 0 || Cq <= 0 || Ck <= 0) return fail(VSA_ERR_INVALID, "%s: B, H, N, Cq, Ck must be positive", fn);
+    if (!blocks) return fail(VSA_ERR_INVALID, "%s: null blocks", fn);
+    const bool has_mask = blocks->mask != nullptr;
+    const bool has_list = blocks->kv_idx != nullptr || blocks->kv_cnt != nullptr;
+    if (has_mask == has_list) return fail(VSA_ERR_INVALID, "%s: give exactly one of mask or (kv_idx, kv_cnt)", fn);
+    if (has_list && (!blocks->kv_idx || !blocks->kv_cnt || blocks->max_kv <= 0))
+        return fail(VSA_ERR_INVALID, "%s: list form needs kv_idx, kv_cnt and max_kv > 0", fn);
+    if (!(scale > 0.f) || !__builtin_isfinite(scale)) return fail(VSA_ERR_INVALID, "%s: scale must be positive and finite", fn);
+    if (dtype != VSA_BF16 || D != 128) return fail(VSA_ERR_UNSUPPORTED, "%s: needs bf16 with D = 128", fn);
+    if (has_mask && Ck > kVarMaxMask) return fail(VSA_ERR_UNSUPPORTED, "%s: mask form supports at most %d key clusters", fn, kVarMaxMask);
+    const int64_t BH = (int64_t)B * H;
+    const int max_chunks = N / kVarBS + Cq;              // sum over clusters of ceil(n / 128) never exceeds this
+    const int max_entries = has_mask ? Ck : blocks->max_kv;
+    const int max_subs = (N + kVarKT - 1) / kVarKT;
+    const size_t shm = ((size_t)(2 * max_entries + 1 + max_subs) * 4 + (has_mask ? (size_t)Ck * 2 : 0) + 15) & ~(size_t)15;
+    if (shm > 64 * 1024) return fail(VSA_ERR_UNSUPPORTED, "%s: block lists too long for one workgroup", fn);
+    if (BH * max_chunks >= (1ll << 31) || (int64_t)N * D * 2 >= (1ll << 31))
+        return fail(VSA_ERR_INVALID, "%s: problem too large", fn);
+    const size_t need = vsa_varlen_attn_workspace_bytes(B, H, Cq);
+    if (!workspace || ws_bytes < need)
+        return fail(VSA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed (got %zu)", fn, need, ws_bytes);
+    VarArgs a{};
+    a.q = static_cast<const uint16_t*>(q);
+    a.k = static_cast<const uint16_t*>(k);
+    a.v = static_cast<const uint16_t*>(v);
+    a.o = static_cast<uint16_t*>(o);
+    a.lse = lse;
+    a.q_off = q_off;
+    a.k_off = k_off;
+    a.mask = blocks->mask;
+    a.kv_idx = blocks->kv_idx;
+    a.kv_cnt = blocks->kv_cnt;
+    a.max_kv = has_list ? blocks->max_kv : 0;
+    a.chunk_start = static_cast<const int32_t*>(workspace);
+    a.N = N; a.Cq = Cq; a.Ck = Ck; a.BH = (int32_t)BH;
+    a.max_chunks = max_chunks; a.max_entries = max_entries; a.max_subs = max_subs;
+    a.scale_log2 = (float)((double)scale * 1.4426950408889634);
+    hipStream_t s = as_stream(stream);
+    hipLaunchKernelGGL(varlen_chunks_kernel, dim3((unsigned)BH), dim3(64), 0, s, a, static_cast<int32_t*>(workspace));
+    hipLaunchKernelGGL(attn_varlen_kernel, dim3((unsigned)(BH * max_chunks)), dim3(256), shm, s, a);
+    return launch_status(fn);
+}

@@ -11,6 +11,9 @@ their outputs; every step runs in a HIP kernel.
   the top-p budget of the Sparse VideoGen2 page, Abstract.
 * long_layer: machinebrief LVSA article (block-sparse attention at a long
   horizon): a local window forced, the rest of a fixed budget by pooled score.
+* semantic_layer: Sparse VideoGen2 page, Abstract: k-means of Q and K per head,
+  cluster-major storage, size-weighted top-p over cluster pairs, attention over
+  the kept clusters without padding, and O moved back to natural order.
 """
 from __future__ import annotations
 
@@ -19,7 +22,8 @@ import math
 from . import (VSA_PATTERN_SPATIAL, VSA_PATTERN_TEMPORAL, VSA_PERM_CUBE4, VSA_PERM_FRAME_MAJOR,
                vsa_block_scores, vsa_block_sparse_attn_fwd, vsa_block_sparse_attn_fwd_chosen,
                vsa_cube_block_len, vsa_cube_dims, vsa_mask_to_list,
-               vsa_pattern_mask, vsa_permute, vsa_profile_heads, vsa_select_topk)
+               vsa_pattern_mask, vsa_permute, vsa_profile_heads, vsa_select_topk, vsa_kmeans,
+               vsa_cluster_order, vsa_gather_rows, vsa_cluster_scores, vsa_varlen_sparse_attn_fwd)
 
 
 def svg_masks(grid, bs, w_spatial, w_temporal, device="cuda"):
@@ -100,4 +104,23 @@ def long_layer(q, k, v, grid, bs, w_local, k_total, scale=None, stats=None):
     o = vsa_block_sparse_attn_fwd(q, k, v, bs, kv_idx=idx, kv_cnt=cnt, scale=scale)
     if stats is not None:
         stats.update(kv_idx=idx, kv_cnt=cnt, forced=forced, scores=S)
+    return o
+
+
+def semantic_layer(q, k, v, Cq, Ck, iters, top_p, k_max=None, scale=None, stats=None):
+    """Returns o in natural order; `stats` receives the intermediate tensors."""
+    cq, lq, nq = vsa_kmeans(q, Cq, iters)
+    ck, lk, nk = vsa_kmeans(k, Ck, iters)
+    pq, oq = vsa_cluster_order(lq, nq)
+    pk, ok = vsa_cluster_order(lk, nk)
+    qs = vsa_gather_rows(q, pq)
+    ks = vsa_gather_rows(k, pk)
+    vs = vsa_gather_rows(v, pk)
+    S = vsa_cluster_scores(cq, ck, nk, scale=scale)
+    idx, cnt = vsa_select_topk(S, Ck if k_max is None else k_max, top_p)
+    os_ = vsa_varlen_sparse_attn_fwd(qs, ks, vs, oq, ok, kv_idx=idx, kv_cnt=cnt, scale=scale)
+    o = vsa_gather_rows(os_, pq, inverse=True)
+    if stats is not None:
+        stats.update(q_centroids=cq, k_centroids=ck, q_labels=lq, k_labels=lk, q_counts=nq, k_counts=nk,
+                     q_perm=pq, k_perm=pk, q_off=oq, k_off=ok, scores=S, kv_idx=idx, kv_cnt=cnt)
     return o

@@ -295,6 +295,88 @@ int vsa_block_sparse_attn_bwd(const void* q, const void* k, const void* v, const
                               const int32_t* blk_len, const vsa_blocks* blocks, float scale,
                               void* workspace, size_t ws_bytes, void* stream);
 
+/* ---- Semantic-aware permutation ------------------------------------------
+ * Sparse VideoGen2 page, Abstract: tokens are clustered by semantic similarity
+ * with k-means and reordered so that every cluster is contiguous; cluster means
+ * stand for their tokens when a top-p budget picks the critical clusters, and
+ * the attention over the kept clusters runs without padding. The flow is
+ *   vsa_kmeans (Q, then K) -> vsa_cluster_order -> vsa_gather_rows (Q by the
+ *   query order, K and V by the key order) -> vsa_cluster_scores ->
+ *   vsa_select_topk (nqb = Cq, nkb = Ck) -> vsa_varlen_sparse_attn_fwd ->
+ *   vsa_gather_rows(inverse = 1) on O. */
+
+/* Lloyd's k-means of the N tokens of every (b, h), C clusters, `iters`
+ * iterations. Seeds: the tokens at positions floor(c N / C). An iteration sends
+ * every token to argmin_c ||m_c||^2 - 2 <x, m_c>, m_c the centroid rounded to
+ * bf16 (fp32 accumulation, ties to the lower index), then replaces each
+ * centroid by the mean of its members (fp32; an empty cluster keeps its
+ * centroid). Deterministic: no floating-point atomics.
+ *   x          [B, H, N, D] bf16, D = 128 (otherwise VSA_ERR_UNSUPPORTED)
+ *   C          1 <= C <= min(N, 4096)
+ *   centroids  out, device fp32 [B, H, C, D]: the means of the final assignment
+ *   labels     out, device int32 [B, H, N]: the final assignment
+ *   counts     out, device int32 [B, H, C]: cluster sizes of the final assignment
+ *   workspace  >= vsa_kmeans_workspace_bytes(B, H, C, D) bytes (bf16 centroids
+ *              and their norms) */
+size_t vsa_kmeans_workspace_bytes(int B, int H, int C, int D);
+int vsa_kmeans(const void* x, int B, int H, int N, int D, int dtype, int C, int iters, float* centroids,
+               int32_t* labels, int32_t* counts, void* workspace, size_t ws_bytes, void* stream);
+
+/* Stable cluster-major order of every (b, h): tokens sorted by label, members of
+ * a cluster in natural order. Integer work, bit-exact.
+ *   labels   device int32 [B, H, N], entries in [0, C) (others are left out)
+ *   counts   device int32 [B, H, C]: the label counts (as from vsa_kmeans)
+ *   C        1 <= C <= 1024
+ *   perm     out, device int32 [B, H, N]: perm[p] = token stored at position p
+ *   offsets  out, device int32 [B, H, C + 1]: cluster c occupies positions
+ *            [offsets[c], offsets[c + 1])
+ *   workspace >= vsa_cluster_order_workspace_bytes(B, H, N, C) bytes */
+size_t vsa_cluster_order_workspace_bytes(int B, int H, int N, int C);
+int vsa_cluster_order(const int32_t* labels, const int32_t* counts, int B, int H, int N, int C,
+                      int32_t* perm, int32_t* offsets, void* workspace, size_t ws_bytes, void* stream);
+
+/* Row gather by a per-head index list (bit-exact data movement):
+ *   inverse = 0: dst[b, h, r] = src[b, h, perm[b, h, r]]
+ *   inverse = 1: dst[b, h, perm[b, h, r]] = src[b, h, r]
+ *   src, dst  [B, H, N, D], bf16 or fp32, D in {64, 128}; must not overlap
+ *   perm      device int32 [B, H, N], a permutation of [0, N) per head (an entry
+ *             outside [0, N) moves nothing) */
+int vsa_gather_rows(const void* src, void* dst, int B, int H, int N, int D, int dtype,
+                    const int32_t* perm, int inverse, void* stream);
+
+/* Size-weighted cluster-pair scores, fp32:
+ *   scores[b, h, a, c] = scale * <cq[b, h, a], ck[b, h, c]> + log(k_counts[b, h, c])
+ * and -inf for an empty key cluster. The softmax of a row is the share of query
+ * cluster a's attention that key cluster c would take if every key equalled its
+ * centroid, so top-p on these scores (vsa_select_topk) weighs clusters by size.
+ *   cq [B, H, Cq, D], ck [B, H, Ck, D] device fp32 (ck 16-byte aligned), D in {64, 128}
+ *   k_counts device int32 [B, H, Ck]; scores out, device fp32 [B, H, Cq, Ck] */
+int vsa_cluster_scores(const float* cq, const float* ck, const int32_t* k_counts, int B, int H,
+                       int Cq, int Ck, int D, float scale, float* scores, void* stream);
+
+/* Attention over variable-size clusters in cluster-major storage. Query cluster
+ * a is rows [q_off[a], q_off[a + 1]) of q, key cluster c rows [k_off[c],
+ * k_off[c + 1]) of k and v; each query of cluster a attends (softmax over all of
+ * them) to the keys of the key clusters kept for a. No padding: the kept key
+ * clusters are packed end to end into 64-key tiles.
+ *   q, k, v, o  [B, H, N, D] bf16, D = 128 (otherwise VSA_ERR_UNSUPPORTED); o is
+ *               written for every row of every query cluster
+ *   lse         optional out, device fp32 [B, H, N]
+ *   q_off       device int32 [B, H, Cq + 1], non-decreasing, q_off[0] = 0,
+ *               q_off[Cq] <= N; k_off likewise [B, H, Ck + 1]
+ *   blocks      host pointer, the kept key clusters of each query cluster: mask
+ *               uint8 [B, H, Cq, Ck] (Ck <= 4096), or kv_idx int32
+ *               [B, H, Cq, max_kv] + kv_cnt [B, H, Cq] with distinct entries in
+ *               [0, Ck), used in the order given (ascending = the mask form's order)
+ *   workspace   >= vsa_varlen_attn_workspace_bytes(B, H, Cq) bytes
+ * Precision as vsa_block_sparse_attn_fwd. A query whose kept clusters hold no key
+ * gets O = 0, LSE = -inf. */
+size_t vsa_varlen_attn_workspace_bytes(int B, int H, int Cq);
+int vsa_varlen_sparse_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                               int B, int H, int N, int D, int dtype, const int32_t* q_off, int Cq,
+                               const int32_t* k_off, int Ck, const vsa_blocks* blocks, float scale,
+                               void* workspace, size_t ws_bytes, void* stream);
+
 /* Validates a block list held in HOST memory: every kv_cnt in [0, max_kv], the
  * first kv_cnt entries of each row strictly ascending and inside [0, nkb).
  * Returns VSA_OK or VSA_ERR_INVALID (message names the first bad row). */

@@ -77,7 +77,13 @@ LONG126 = Workload("long_horizon_126x30x52", B=1, H=12, D=128, T=126, Hh=30, W=5
                    dtype="bf16", seed=4, generator="sinusoid_outliers",
                    extra=dict(w_local=1, density=0.10, outlier_frac=0.03, outlier_logit=3.0))
 
-ALL = [TINY, WAN480, HUNYUAN720, WAN480_CUBE, LONG126]
+# Sparse VideoGen2-style layer on the Wan shape: 64 spatially coherent semantic
+# components, k-means with 128 query and 256 key clusters, size-weighted top-p 0.9.
+WAN480_SEMANTIC = Workload("wan2.1_480p_semantic", B=1, H=12, D=128, T=21, Hh=30, W=52, bs=128,
+                           dtype="bf16", seed=5, generator="mixture",
+                           extra=dict(n_components=64, mean_scale=0.75, Cq=128, Ck=256, iters=3, top_p=0.9))
+
+ALL = [TINY, WAN480, HUNYUAN720, WAN480_CUBE, LONG126, WAN480_SEMANTIC]
 BY_NAME = {w.name: w for w in ALL}
 
 
