@@ -30,7 +30,7 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-from workloads import WAN480, WAN480_CUBE, LONG126, make_qkv, profile_rows  # noqa: E402
+from workloads import WAN480, WAN480_CUBE, WAN480_SEMANTIC, LONG126, make_qkv, profile_rows  # noqa: E402
 
 PEAK_BF16_TFLOPS = 2516.6       # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
@@ -510,6 +510,52 @@ def extra_layers(torch, V, PL, T):
                                      "k_total": k_total, "attn_tflops": round(fl / (t_att * 1e-3) / 1e12, 2),
                                      "pct_mfma_peak": round(100 * fl / (t_att * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2)}
     del q, k, v, o, S
+    torch.cuda.empty_cache()
+
+    # Sparse VideoGen2-style layer: k-means of Q and K, cluster-major storage,
+    # size-weighted top-p, attention over the kept clusters, O moved back
+    w = WAN480_SEMANTIC
+    q, k, v = (torch.from_numpy(x).to(torch.bfloat16).to(dev) for x in make_qkv(w))
+    Cq, Ck, iters, top_p = w.extra["Cq"], w.extra["Ck"], w.extra["iters"], w.extra["top_p"]
+    times = {}
+    for rep in range(4):
+        e = [T.ev()]
+        cq, lq, nq = V.vsa_kmeans(q, Cq, iters)
+        e.append(T.ev())
+        ck, lk, nk = V.vsa_kmeans(k, Ck, iters)
+        e.append(T.ev())
+        pq, oq = V.vsa_cluster_order(lq, Cq)
+        pk, ok = V.vsa_cluster_order(lk, Ck)
+        e.append(T.ev())
+        qs = V.vsa_gather_rows(q, pq)
+        ks = V.vsa_gather_rows(k, pk)
+        vs = V.vsa_gather_rows(v, pk)
+        e.append(T.ev())
+        S = V.vsa_cluster_scores(cq, ck, nk)
+        idx, cnt = V.vsa_select_topk(S, Ck, top_p)
+        e.append(T.ev())
+        os_ = V.vsa_varlen_sparse_attn_fwd(qs, ks, vs, oq, ok, kv_idx=idx, kv_cnt=cnt)
+        e.append(T.ev())
+        o = V.vsa_gather_rows(os_, pq, inverse=True)
+        e.append(T.ev())
+        torch.cuda.synchronize()
+        if rep:
+            for key, i in (("kmeans_q", 0), ("kmeans_k", 1), ("cluster_order_qk", 2), ("gather_qkv", 3),
+                           ("scores_select", 4), ("varlen_attention", 5), ("gather_o", 6)):
+                times.setdefault(key, []).append(e[i].elapsed_time(e[i + 1]))
+    nqh, nkh, ih, ch = (x.cpu().numpy().astype(np.int64) for x in (nq, nk, idx, cnt))
+    kept = 0.0
+    for h in range(w.H):
+        for a in range(Cq):
+            kept += float(nqh[0, h, a]) * float(nkh[0, h, ih[0, h, a, :ch[0, h, a]]].sum())
+    fl = 4.0 * w.D * kept
+    ms = {k_: round(float(np.mean(v_)), 4) for k_, v_ in times.items()}
+    t_att = ms["varlen_attention"]
+    res["semantic_wan480"] = {"ms": ms, "total_ms": round(sum(ms.values()), 4), "Cq": Cq, "Ck": Ck, "iters": iters,
+                              "top_p": top_p, "kept_pair_density": round(kept / (w.H * w.N * w.N), 4),
+                              "kept_flops": fl, "attn_tflops": round(fl / (t_att * 1e-3) / 1e12, 2),
+                              "pct_mfma_peak": round(100 * fl / (t_att * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2)}
+    del q, k, v, qs, ks, vs, os_, o, S
     torch.cuda.empty_cache()
     return res
 

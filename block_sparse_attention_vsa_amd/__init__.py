@@ -64,13 +64,13 @@ _SIGNATURES = {
     "vsa_attn_bwd_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I]),
     "vsa_block_sparse_attn_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P,
                                        ctypes.POINTER(vsa_blocks), _F, _P, _SZ, _P]),
-    "vsa_kmeans_workspace_bytes": (_SZ, [_I, _I, _I, _I]),
+    "vsa_kmeans_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I]),
     "vsa_kmeans": (_I, [_P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _SZ, _P]),
     "vsa_cluster_order_workspace_bytes": (_SZ, [_I, _I, _I, _I]),
-    "vsa_cluster_order": (_I, [_P, _P, _I, _I, _I, _I, _P, _P, _P, _SZ, _P]),
+    "vsa_cluster_order": (_I, [_P, _I, _I, _I, _I, _P, _P, _P, _SZ, _P]),
     "vsa_gather_rows": (_I, [_P, _P, _I, _I, _I, _I, _I, _P, _I, _P]),
     "vsa_cluster_scores": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _F, _P, _P]),
-    "vsa_varlen_attn_workspace_bytes": (_SZ, [_I, _I, _I]),
+    "vsa_varlen_attn_workspace_bytes": (_SZ, [_I, _I, _I, _I]),
     "vsa_varlen_sparse_attn_fwd": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _I, _P, _I,
                                         ctypes.POINTER(vsa_blocks), _F, _P, _SZ, _P]),
     "vsa_check_block_list_host": (_I, [_P, _P, _I64, _I, _I]),
@@ -462,8 +462,8 @@ def vsa_block_sparse_attn_bwd(q, k, v, o, lse, dout, bs: int, mask=None, kv_idx=
     return dq, dk, dv
 
 
-def vsa_kmeans_workspace_bytes(B, H, C, D) -> int:
-    return lib().vsa_kmeans_workspace_bytes(B, H, C, D)
+def vsa_kmeans_workspace_bytes(B, H, N, C, D) -> int:
+    return lib().vsa_kmeans_workspace_bytes(B, H, N, C, D)
 
 
 def vsa_kmeans(x, C: int, iters: int, out=None, workspace=None):
@@ -478,7 +478,7 @@ def vsa_kmeans(x, C: int, iters: int, out=None, workspace=None):
                torch.empty((B, H, C), dtype=torch.int32, device=x.device))
     cent, lab, cnt = out
     if workspace is None:
-        workspace = torch.empty((max(1, vsa_kmeans_workspace_bytes(B, H, C, D)),), dtype=torch.uint8,
+        workspace = torch.empty((max(1, vsa_kmeans_workspace_bytes(B, H, N, C, D)),), dtype=torch.uint8,
                                 device=x.device)
     _check(lib().vsa_kmeans(_ptr(x), B, H, N, D, _dtype_code(x), C, iters, _ptr(cent), _ptr(lab), _ptr(cnt),
                             _ptr(workspace), workspace.numel(), _stream(x.device)), "vsa_kmeans")
@@ -489,13 +489,11 @@ def vsa_cluster_order_workspace_bytes(B, H, N, C) -> int:
     return lib().vsa_cluster_order_workspace_bytes(B, H, N, C)
 
 
-def vsa_cluster_order(labels, counts, out=None, workspace=None):
+def vsa_cluster_order(labels, C: int, out=None, workspace=None):
     """Stable cluster-major order: (perm int32 [B, H, N], offsets int32 [B, H, C + 1])."""
     torch = _torch()
     _need(labels, "labels", torch.int32, 3)
-    _need(counts, "counts", torch.int32, 3)
     B, H, N = labels.shape
-    C = counts.shape[-1]
     if out is None:
         out = (torch.empty((B, H, N), dtype=torch.int32, device=labels.device),
                torch.empty((B, H, C + 1), dtype=torch.int32, device=labels.device))
@@ -503,7 +501,7 @@ def vsa_cluster_order(labels, counts, out=None, workspace=None):
     if workspace is None:
         workspace = torch.empty((max(1, vsa_cluster_order_workspace_bytes(B, H, N, C)),), dtype=torch.uint8,
                                 device=labels.device)
-    _check(lib().vsa_cluster_order(_ptr(labels), _ptr(counts), B, H, N, C, _ptr(perm), _ptr(off), _ptr(workspace),
+    _check(lib().vsa_cluster_order(_ptr(labels), B, H, N, C, _ptr(perm), _ptr(off), _ptr(workspace),
                                    workspace.numel(), _stream(labels.device)), "vsa_cluster_order")
     return perm, off
 
@@ -535,8 +533,8 @@ def vsa_cluster_scores(cq, ck, k_counts, scale=None, out=None):
     return out
 
 
-def vsa_varlen_attn_workspace_bytes(B, H, Cq) -> int:
-    return lib().vsa_varlen_attn_workspace_bytes(B, H, Cq)
+def vsa_varlen_attn_workspace_bytes(B, H, N, Cq) -> int:
+    return lib().vsa_varlen_attn_workspace_bytes(B, H, N, Cq)
 
 
 def vsa_varlen_sparse_attn_fwd(q, k, v, q_off, k_off, mask=None, kv_idx=None, kv_cnt=None, scale=None,
@@ -558,7 +556,7 @@ def vsa_varlen_sparse_attn_fwd(q, k, v, q_off, k_off, mask=None, kv_idx=None, kv
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     blocks = _blocks_arg(q, 0, mask, kv_idx, kv_cnt)
     if workspace is None:
-        workspace = torch.empty((vsa_varlen_attn_workspace_bytes(B, H, Cq),), dtype=torch.uint8, device=q.device)
+        workspace = torch.empty((vsa_varlen_attn_workspace_bytes(B, H, N, Cq),), dtype=torch.uint8, device=q.device)
     _check(lib().vsa_varlen_sparse_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, N, D,
                                             _dtype_code(q), _ptr(q_off), Cq, _ptr(k_off), Ck, ctypes.byref(blocks),
                                             scale, _ptr(workspace), workspace.numel(), _stream(q.device)),

@@ -8,12 +8,14 @@
 //   O_i = sum_{j in kept clusters of a} softmax_j(scale <q_i, k_j>) v_j.
 //
 // One workgroup per (b, h, query cluster, chunk of at most 128 rows), 4 waves of
-// 32 rows, Q in registers. The kept key clusters are laid end to end into one
-// packed key sequence, walked in 64-key sub-tiles: every DMA lane maps its
-// packed position to a row of K / V (a per-workgroup LDS table holds each kept
-// cluster's packed start and row start, and each sub-tile's first cluster), so
-// clusters of any size share sub-tiles and only the last sub-tile of a
-// workgroup is partial. The score / softmax / P V core is the one of the block
+// 32 rows, Q in registers; the chunks are launched in descending order of their
+// kept-key counts, which vary by two orders of magnitude between clusters. The
+// kept key clusters are laid end to end into one packed key sequence, walked in
+// 64-key sub-tiles: every DMA lane maps its packed position to a row of K / V
+// through a per-workgroup LDS table (row minus position for each 16-key group
+// inside one cluster; a short walk over the clusters' packed starts for a group
+// that spans two), so clusters of any size share sub-tiles and only the last
+// sub-tile of a workgroup is partial. The score / softmax / P V core is the one of the block
 // kernel (S^T = K Q^T on v_mfma_f32_32x32x16_bf16, online softmax in the log2
 // domain with a lazily moved offset, V^T through transposing LDS reads).
 #include <math.h>
@@ -39,6 +41,9 @@ struct VarArgs {
     const int32_t* kv_cnt;         // [BH, Cq]
     int32_t max_kv;
     const int32_t* chunk_start;    // [BH, Cq + 1]: first chunk of each query cluster
+    int32_t* work;                 // [BH, Cq]: keys kept by each query cluster
+    int32_t* order;                // [BH max_chunks]: launch order of the chunks (heaviest first)
+    int32_t* n_items;              // [1]: number of chunks
     int32_t N, Cq, Ck, BH, max_chunks, max_entries, max_subs;
     float scale_log2;
 };
@@ -67,6 +72,72 @@ __global__ __launch_bounds__(64) void varlen_chunks_kernel(VarArgs a, int32_t* c
         run += __shfl(x, 63);
     }
     if (lane == 0) out[a.Cq] = run;
+}
+
+// keys kept by each query cluster: one wave per (b, h, query cluster)
+__global__ __launch_bounds__(256) void varlen_work_kernel(VarArgs a) {
+    const int64_t g = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (g >= (int64_t)a.BH * a.Cq) return;
+    const int64_t bh = g / a.Cq;
+    const int32_t* ko = a.k_off + bh * (a.Ck + 1);
+    int64_t keys = 0;
+    if (a.mask) {
+        const uint8_t* row = a.mask + g * a.Ck;
+        for (int c = lane; c < a.Ck; c += 64)
+            if (row[c]) keys += ko[c + 1] - ko[c];
+    } else {
+        const int cnt = min(a.kv_cnt[g], a.max_kv);
+        const int32_t* idx = a.kv_idx + g * a.max_kv;
+        for (int e = lane; e < cnt; e += 64) {
+            const int c = idx[e];
+            if ((unsigned)c < (unsigned)a.Ck) keys += ko[c + 1] - ko[c];
+        }
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) keys += __shfl_xor(keys, off);
+    if (lane == 0) a.work[g] = (int32_t)min<int64_t>(keys, 0x7fffffff);
+}
+
+// Launch order: every chunk of every query cluster, by descending kept-key count
+// (256 buckets of a counting sort in one workgroup), so that the longest
+// workgroups start first. Only the schedule depends on it (the order inside a
+// bucket comes from LDS integer atomics); no result does.
+__global__ __launch_bounds__(1024) void varlen_order_kernel(VarArgs a) {
+    __shared__ int hist[256];
+    const int t = threadIdx.x;
+    const int pairs = a.BH * a.Cq;
+    if (t < 256) hist[t] = 0;
+    __syncthreads();
+    auto bucket = [&](int g) {
+        const int64_t b = (int64_t)a.work[g] * 255 / max(a.N, 1);
+        return 255 - (int)min<int64_t>(b, 255);
+    };
+    auto chunks = [&](int g) {
+        const int bh = g / a.Cq, c = g - bh * a.Cq;
+        const int32_t* cs = a.chunk_start + (int64_t)bh * (a.Cq + 1);
+        return cs[c + 1] - cs[c];
+    };
+    for (int g = t; g < pairs; g += 1024) atomicAdd(&hist[bucket(g)], chunks(g));
+    __syncthreads();
+    if (t == 0) {
+        int run = 0;
+        for (int b = 0; b < 256; ++b) {
+            const int h = hist[b];
+            hist[b] = run;
+            run += h;
+        }
+        *a.n_items = run;
+    }
+    __syncthreads();
+    for (int g = t; g < pairs; g += 1024) {
+        const int n = chunks(g);
+        if (n <= 0) continue;
+        const int pos = atomicAdd(&hist[bucket(g)], n);
+        const int bh = g / a.Cq, c = g - bh * a.Cq;
+        const int first = a.chunk_start[(int64_t)bh * (a.Cq + 1) + c];
+        for (int u = 0; u < n; ++u) a.order[pos + u] = bh * a.max_chunks + first + u;
+    }
 }
 
 // Exclusive scan of one value per thread over a 256-thread workgroup; returns
@@ -102,19 +173,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
     __shared__ __attribute__((aligned(1024))) uint8_t v1[SUBB];
     __shared__ int scan_tmp[4];
     __shared__ int wave_cnt[WAVES];
-    // dynamic: pp[max_entries + 1] | kst[max_entries] | t0[max_subs] | list16[Ck] (mask form)
+    // dynamic: pp[max_entries + 1] | kst[max_entries] | t0[max_subs] | gd[4 max_subs] | list16[Ck] (mask form)
     extern __shared__ __attribute__((aligned(16))) int32_t dyn[];
     int32_t* pp = dyn;
     int32_t* kst = pp + a.max_entries + 1;
     int32_t* t0 = kst + a.max_entries;
-    int16_t* list16 = reinterpret_cast<int16_t*>(t0 + a.max_subs);
+    int32_t* gd = t0 + a.max_subs;
+    int16_t* list16 = reinterpret_cast<int16_t*>(gd + 4 * a.max_subs);
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int l32 = lane & 31, half = lane >> 5;
-    const int item = xcd_remap(blockIdx.x, a.BH * a.max_chunks);
+    if ((int)blockIdx.x >= ld_const(a.n_items, 0)) return;     // past the last chunk (uniform)
+    const int item = ld_const(a.order, (int)blockIdx.x);
     const int bh = item / a.max_chunks, ci = item - bh * a.max_chunks;
     const int32_t* cs = a.chunk_start + (int64_t)bh * (a.Cq + 1);
-    if (ci >= ld_const(cs, a.Cq)) return;                      // past this head's chunks (uniform)
     int lo = 0, hi = a.Cq;                                      // cs[lo] <= ci < cs[hi]
     while (hi - lo > 1) {
         const int mid = (lo + hi) >> 1;
@@ -162,9 +234,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
     L = min(L, a.max_subs * KT);          // repeated clusters cannot overrun the table
     if (tid == 0) pp[cnt] = L;
     __syncthreads();
+    // t0: first entry of each sub-tile; gd: row - position for every 16-key group
+    // that lies inside one entry, INT_MIN for a group that spans entries
     for (int e = tid; e < cnt; e += THREADS) {
         const int p0 = pp[e], p1 = min(pp[e + 1], L);
+        if (p1 <= p0) continue;
         for (int i = (p0 + KT - 1) / KT; i * KT < p1; ++i) t0[i] = e;
+        for (int g = p0 >> 4; g <= (p1 - 1) >> 4; ++g)
+            gd[g] = (16 * g >= p0 && 16 * g + 16 <= p1) ? kst[e] - p0 : INT_MIN;
     }
     __syncthreads();
     const int n_sub = (L + KT - 1) / KT;
@@ -172,15 +249,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
     const SubTileDma<WAVES, kVSwz4, KT> dma(lane, w);
     const int head_bytes = a.N * D * 2;
     auto issue = [&](int i, uint8_t* kd, uint8_t* vd) {
-        int e = t0[i];
 #pragma unroll
         for (int u = 0; u < SubTileDma<WAVES, kVSwz4, KT>::IPW; ++u) {
             const int ins = w + WAVES * u;
-            const int p = i * KT + 4 * ins + (lane >> 4);
+            const int p = i * KT + 4 * ins + (lane >> 4);     // 16-key group 4 i + u
             int row = a.N;                                      // past the head: reads zeros
             if (p < L) {
-                while (e + 1 < cnt && pp[e + 1] <= p) ++e;
-                row = kst[e] + (p - pp[e]);
+                const int d = gd[p >> 4];
+                if (d != INT_MIN) {
+                    row = d + p;
+                } else {                                        // the group spans entries: walk
+                    int e = t0[i];
+                    while (e + 1 < cnt && pp[e + 1] <= p) ++e;
+                    row = kst[e] + (p - pp[e]);
+                }
             }
             dma16(a.k + head_off, head_bytes, kd + ins * 1024, row * 256 + dma.ck[u % SubTileDma<WAVES, kVSwz4, KT>::NCLS], 0);
             dma16(a.v + head_off, head_bytes, vd + ins * 1024, row * 256 + dma.cv, 0);
@@ -291,9 +373,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
 
 using namespace vsa;
 
-extern "C" size_t vsa_varlen_attn_workspace_bytes(int B, int H, int Cq) {
-    if (B <= 0 || H <= 0 || Cq <= 0) return 0;
-    return (size_t)B * H * (Cq + 1) * 4;
+struct VarPlan {
+    size_t off_cs, off_work, off_order, off_n, total;
+};
+
+static VarPlan varlen_plan(int64_t BH, int N, int Cq) {
+    VarPlan p;
+    const int64_t max_chunks = N / kVarBS + Cq;
+    auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
+    p.off_cs = 0;
+    p.off_work = al((size_t)BH * (Cq + 1) * 4);
+    p.off_order = p.off_work + al((size_t)BH * Cq * 4);
+    p.off_n = p.off_order + al((size_t)BH * max_chunks * 4);
+    p.total = p.off_n + 256;
+    return p;
+}
+
+extern "C" size_t vsa_varlen_attn_workspace_bytes(int B, int H, int N, int Cq) {
+    if (B <= 0 || H <= 0 || N <= 0 || Cq <= 0) return 0;
+    return varlen_plan((int64_t)B * H, N, Cq).total;
 }
 
 extern "C" int vsa_varlen_sparse_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B,
@@ -318,11 +416,11 @@ extern "C" int vsa_varlen_sparse_attn_fwd(const void* q, const void* k, const vo
     const int max_chunks = N / kVarBS + Cq;              // sum over clusters of ceil(n / 128) never exceeds this
     const int max_entries = has_mask ? Ck : blocks->max_kv;
     const int max_subs = (N + kVarKT - 1) / kVarKT;
-    const size_t shm = ((size_t)(2 * max_entries + 1 + max_subs) * 4 + (has_mask ? (size_t)Ck * 2 : 0) + 15) & ~(size_t)15;
+    const size_t shm = ((size_t)(2 * max_entries + 1 + 5 * max_subs) * 4 + (has_mask ? (size_t)Ck * 2 : 0) + 15) & ~(size_t)15;
     if (shm > 64 * 1024) return fail(VSA_ERR_UNSUPPORTED, "%s: block lists too long for one workgroup", fn);
     if (BH * max_chunks >= (1ll << 31) || (int64_t)N * D * 2 >= (1ll << 31))
         return fail(VSA_ERR_INVALID, "%s: problem too large", fn);
-    const size_t need = vsa_varlen_attn_workspace_bytes(B, H, Cq);
+    const size_t need = vsa_varlen_attn_workspace_bytes(B, H, N, Cq);
     if (!workspace || ws_bytes < need)
         return fail(VSA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed (got %zu)", fn, need, ws_bytes);
     VarArgs a{};
@@ -337,12 +435,20 @@ extern "C" int vsa_varlen_sparse_attn_fwd(const void* q, const void* k, const vo
     a.kv_idx = blocks->kv_idx;
     a.kv_cnt = blocks->kv_cnt;
     a.max_kv = has_list ? blocks->max_kv : 0;
-    a.chunk_start = static_cast<const int32_t*>(workspace);
+    const VarPlan pl = varlen_plan(BH, N, Cq);
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    a.chunk_start = reinterpret_cast<const int32_t*>(ws + pl.off_cs);
+    a.work = reinterpret_cast<int32_t*>(ws + pl.off_work);
+    a.order = reinterpret_cast<int32_t*>(ws + pl.off_order);
+    a.n_items = reinterpret_cast<int32_t*>(ws + pl.off_n);
     a.N = N; a.Cq = Cq; a.Ck = Ck; a.BH = (int32_t)BH;
     a.max_chunks = max_chunks; a.max_entries = max_entries; a.max_subs = max_subs;
     a.scale_log2 = (float)((double)scale * 1.4426950408889634);
     hipStream_t s = as_stream(stream);
-    hipLaunchKernelGGL(varlen_chunks_kernel, dim3((unsigned)BH), dim3(64), 0, s, a, static_cast<int32_t*>(workspace));
+    hipLaunchKernelGGL(varlen_chunks_kernel, dim3((unsigned)BH), dim3(64), 0, s, a,
+                       reinterpret_cast<int32_t*>(ws + pl.off_cs));
+    hipLaunchKernelGGL(varlen_work_kernel, dim3((unsigned)((BH * Cq + 3) / 4)), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(varlen_order_kernel, dim3(1), dim3(1024), 0, s, a);
     hipLaunchKernelGGL(attn_varlen_kernel, dim3((unsigned)(BH * max_chunks)), dim3(256), shm, s, a);
     return launch_status(fn);
 }

@@ -12,10 +12,12 @@
 //    in 64-row sub-tiles by DMA and the products run on v_mfma_f32_32x32x16_bf16
 //    (the accumulator gives each lane one token and 16 centroids per 32-row half).
 //  * Update: centroid = mean of its members, an empty cluster keeps its value.
-//    A workgroup owns 8 clusters; each of its 16 waves scans one sixteenth of the
-//    tokens in order and accumulates its members in registers; the 16 partial
-//    sums are then added in wave order. No floating-point atomics, so the result
-//    does not depend on scheduling.
+//    Each iteration first puts the tokens in the stable cluster-major order of
+//    the new labels (integer work, below), so every cluster's members are one
+//    contiguous range; a workgroup per cluster sums its range in 32 fixed
+//    streams added in stream order. No floating-point atomics, so the result
+//    does not depend on scheduling, and clusters of any size or spatial spread
+//    cost the same per member.
 //  * Order: stable counting sort by cluster. Chunks of 256 tokens count their
 //    clusters, a per-cluster scan over chunks gives each chunk's first slot, and
 //    every token's rank among equal clusters in its chunk comes from wave ballots.
@@ -26,10 +28,8 @@
 namespace vsa {
 
 constexpr int kKmD = 128;                 // token width handled by the k-means kernels
-constexpr int kKmMaxC = 4096;             // clusters per head
 constexpr int kOrdChunk = 256;            // tokens per counting-sort chunk (4 waves)
 constexpr int kOrdMaxC = 1024;            // clusters per head for the order kernels
-constexpr int kUpdWaves = 16, kUpdClusters = 8;
 
 struct KmArgs {
     const uint16_t* x;        // [BH, N, 128] bf16
@@ -144,90 +144,60 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     if (ok && half == 0) a.labels[(int64_t)bh * a.N + t] = pick;
 }
 
-// ---- update: one workgroup per (bh, 8 clusters), 16 waves over the tokens --------
-__global__ __launch_bounds__(kUpdWaves * 64) void km_update_kernel(KmArgs a, int groups) {
-    __shared__ float part[kUpdWaves][kUpdClusters][kKmD];
-    __shared__ int pcnt[kUpdWaves][kUpdClusters];
-    __shared__ float mb[kUpdClusters][kKmD];
+// ---- update: one workgroup per (bh, cluster) over its members ------------------
+// The members of cluster c are positions [off[c], off[c + 1]) of the stable
+// cluster-major order of the current labels. 32 streams (4 per wave, 16 lanes x
+// 8 channels each) take every 32nd member, the streams' partial sums are added
+// in stream order: a fixed order, independent of scheduling.
+__global__ __launch_bounds__(512) void km_update_kernel(KmArgs a, const int32_t* perm, const int32_t* off) {
+    constexpr int STREAMS = 32, UNROLL = 8;
+    __shared__ float part[STREAMS][kKmD];
+    __shared__ float mb[kKmD];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int item = xcd_remap(blockIdx.x, a.BH * groups);
-    const int64_t bh = item / groups;
-    const int c0 = (item - (int)bh * groups) * kUpdClusters;
-    const int per = ((a.N + kUpdWaves - 1) / kUpdWaves + 63) & ~63;
-    const int t0 = min(a.N, w * per), t1 = min(a.N, t0 + per);
-    const int32_t* lab = a.labels + bh * a.N;
+    const int item = xcd_remap(blockIdx.x, a.BH * a.C);
+    const int64_t bh = item / a.C;
+    const int c = item - (int)bh * a.C;
+    const int32_t* ofs = off + bh * (a.C + 1);
+    const int m0 = ofs[c], m1 = ofs[c + 1];
+    const int stream = 4 * w + (lane >> 4), chunk = lane & 15;     // channels 8 chunk .. 8 chunk + 7
+    const int32_t* ph = perm + bh * a.N;
     const uint16_t* xh = a.x + bh * a.N * kKmD;
-    float acc[kUpdClusters][2];
+    float acc[8];
 #pragma unroll
-    for (int k = 0; k < kUpdClusters; ++k) acc[k][0] = acc[k][1] = 0.f;
-    int cnt[kUpdClusters];
+    for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+    for (int p0 = m0 + stream; p0 < m1; p0 += STREAMS * UNROLL) {
+        int tok[UNROLL];
 #pragma unroll
-    for (int k = 0; k < kUpdClusters; ++k) cnt[k] = 0;
-    for (int base = t0; base < t1; base += 64) {
-        const int t = base + lane;
-        const int rel = (t < t1) ? lab[t] - c0 : -1;
-        uint64_t m = __ballot(rel >= 0 && rel < kUpdClusters);
-        while (m) {
-            // up to four members at a time: their rows load together
-            int j[4], r[4], nm = 0;
+        for (int u = 0; u < UNROLL; ++u) tok[u] = ph[min(p0 + STREAMS * u, m1 - 1)];
+        u32x4 row[UNROLL];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                j[u] = 0;
-                r[u] = 0;
-                if (m) {
-                    j[u] = __builtin_ctzll(m);
-                    m &= m - 1;
-                    r[u] = __builtin_amdgcn_readlane(rel, j[u]);
-                    ++nm;
-                }
-            }
-            uint32_t pr[4];
+        for (int u = 0; u < UNROLL; ++u)
+            row[u] = *reinterpret_cast<const u32x4*>(xh + (int64_t)tok[u] * kKmD + 8 * chunk);
 #pragma unroll
-            for (int u = 0; u < 4; ++u)
-                pr[u] = u < nm ? *reinterpret_cast<const uint32_t*>(xh + (int64_t)(base + j[u]) * kKmD + 2 * lane) : 0u;
+        for (int u = 0; u < UNROLL; ++u) {
+            if (p0 + STREAMS * u >= m1) break;
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                if (u >= nm) break;
-                const float v0 = bf16_bits_to_f32(pr[u] & 0xffffu), v1 = bf16_bits_to_f32(pr[u] >> 16);
-#pragma unroll
-                for (int k = 0; k < kUpdClusters; ++k)
-                    if (r[u] == k) {
-                        acc[k][0] += v0;
-                        acc[k][1] += v1;
-                        ++cnt[k];
-                    }
+            for (int e = 0; e < 4; ++e) {
+                acc[2 * e] += bf16_bits_to_f32(row[u][e] & 0xffffu);
+                acc[2 * e + 1] += bf16_bits_to_f32(row[u][e] >> 16);
             }
         }
     }
 #pragma unroll
-    for (int k = 0; k < kUpdClusters; ++k) {
-        part[w][k][2 * lane] = acc[k][0];
-        part[w][k][2 * lane + 1] = acc[k][1];
-        if (lane == 0) pcnt[w][k] = cnt[k];
+    for (int e = 0; e < 8; ++e) part[stream][8 * chunk + e] = acc[e];
+    __syncthreads();
+    const int64_t row = bh * a.C + c;
+    const int n = m1 - m0;
+    if (tid < kKmD) {
+        float sum = 0.f;
+#pragma unroll
+        for (int u = 0; u < STREAMS; ++u) sum += part[u][tid];
+        mb[tid] = n > 0 ? sum / (float)n : a.cent[row * kKmD + tid];
+        if (tid == 0) a.counts[row] = n;
     }
     __syncthreads();
-    // 8 clusters x 128 channels: thread tid < 1024 takes one value
-    {
-        const int k = tid >> 7, d = tid & 127;
-        const int c = c0 + k;
-        float s = 0.f;
-        int n = 0;
-        for (int u = 0; u < kUpdWaves; ++u) {
-            s += part[u][k][d];
-            n += pcnt[u][k];
-        }
-        float v = 0.f;
-        if (c < a.C) {
-            const int64_t row = bh * a.C + c;
-            v = n > 0 ? s / (float)n : a.cent[row * kKmD + d];
-            if (d == 0) a.counts[row] = n;
-        }
-        mb[k][d] = v;
-    }
-    __syncthreads();
-    if (w < kUpdClusters && c0 + w < a.C) {
-        const int64_t row = bh * a.C + c0 + w;
-        const float nrm = wave_sum(put_centroid(a, row, lane, mb[w][2 * lane], mb[w][2 * lane + 1]));
+    if (w == 0) {
+        const float nrm = wave_sum(put_centroid(a, row, lane, mb[2 * lane], mb[2 * lane + 1]));
         if (lane == 0) a.cnorm[row] = nrm;
     }
 }
@@ -235,34 +205,11 @@ __global__ __launch_bounds__(kUpdWaves * 64) void km_update_kernel(KmArgs a, int
 // ---- stable cluster-major order -------------------------------------------------
 struct OrdArgs {
     const int32_t* labels;    // [BH, N]
-    const int32_t* counts;    // [BH, C]
     int32_t* perm;            // [BH, N]: perm[p] = token at position p
-    int32_t* offsets;         // [BH, C + 1]
-    int32_t* chunk;           // [BH, nch, C]: counts, then first slots
+    int32_t* offsets;         // [BH, C + 1]: cluster sizes, then their exclusive prefix
+    int32_t* chunk;           // [BH, nch, C]: counts, then each chunk's first slot within its cluster
     int32_t N, C, BH, nch;
 };
-
-// cluster offsets: one wave per bh (exclusive scan of the counts)
-__global__ __launch_bounds__(64) void ord_offsets_kernel(OrdArgs a) {
-    const int64_t bh = blockIdx.x;
-    const int lane = threadIdx.x;
-    const int32_t* cnt = a.counts + bh * a.C;
-    int32_t* off = a.offsets + bh * (a.C + 1);
-    int run = 0;
-    for (int c0 = 0; c0 < a.C; c0 += 64) {
-        const int c = c0 + lane;
-        const int v = c < a.C ? cnt[c] : 0;
-        int x = v;
-#pragma unroll
-        for (int d = 1; d < 64; d <<= 1) {
-            const int y = __shfl_up(x, d);
-            if (lane >= d) x += y;
-        }
-        if (c < a.C) off[c] = run + x - v;
-        run += __shfl(x, 63);
-    }
-    if (lane == 0) off[a.C] = run;
-}
 
 // per-chunk cluster counts (LDS integer histogram; counts do not depend on order)
 __global__ __launch_bounds__(kOrdChunk) void ord_count_kernel(OrdArgs a) {
@@ -281,14 +228,15 @@ __global__ __launch_bounds__(kOrdChunk) void ord_count_kernel(OrdArgs a) {
     for (int c = threadIdx.x; c < a.C; c += kOrdChunk) out[c] = hist[c];
 }
 
-// first slot of every (chunk, cluster): one wave per (bh, c), scanning the chunks
+// each chunk's first slot within its cluster, and the cluster sizes: one wave
+// per (bh, c), scanning the chunks
 __global__ __launch_bounds__(256) void ord_scan_kernel(OrdArgs a) {
     const int64_t g = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     if (g >= (int64_t)a.BH * a.C) return;
     const int64_t bh = g / a.C;
     const int c = (int)(g - bh * a.C);
-    int run = a.offsets[bh * (a.C + 1) + c];
+    int run = 0;
     for (int c0 = 0; c0 < a.nch; c0 += 64) {
         const int ch = c0 + lane;
         int32_t* p = a.chunk + (bh * a.nch + ch) * a.C + c;
@@ -302,9 +250,31 @@ __global__ __launch_bounds__(256) void ord_scan_kernel(OrdArgs a) {
         if (ch < a.nch) *p = run + x - v;
         run += __shfl(x, 63);
     }
+    if (lane == 0) a.offsets[bh * (a.C + 1) + c] = run;
 }
 
-// scatter: position = first slot of (chunk, cluster) + rank in the chunk
+// cluster sizes -> offsets, in place: one wave per bh (exclusive scan)
+__global__ __launch_bounds__(64) void ord_offsets_kernel(OrdArgs a) {
+    const int64_t bh = blockIdx.x;
+    const int lane = threadIdx.x;
+    int32_t* off = a.offsets + bh * (a.C + 1);
+    int run = 0;
+    for (int c0 = 0; c0 < a.C; c0 += 64) {
+        const int c = c0 + lane;
+        const int v = c < a.C ? off[c] : 0;
+        int x = v;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int y = __shfl_up(x, d);
+            if (lane >= d) x += y;
+        }
+        if (c < a.C) off[c] = run + x - v;
+        run += __shfl(x, 63);
+    }
+    if (lane == 0) off[a.C] = run;
+}
+
+// scatter: position = cluster offset + the chunk's first slot + rank in the chunk
 __global__ __launch_bounds__(kOrdChunk) void ord_scatter_kernel(OrdArgs a) {
     constexpr int WAVES = kOrdChunk / 64;
     __shared__ int wcnt[WAVES][kOrdMaxC];
@@ -331,9 +301,17 @@ __global__ __launch_bounds__(kOrdChunk) void ord_scatter_kernel(OrdArgs a) {
     if (ok) {
         int before = 0;
         for (int u = 0; u < w; ++u) before += wcnt[u][l];
-        const int pos = a.chunk[(bh * a.nch + ch) * a.C + l] + before + rank;
-        if ((unsigned)pos < (unsigned)a.N) a.perm[bh * a.N + pos] = t;   // counts that disagree with the labels
+        const int pos = a.offsets[bh * (a.C + 1) + l] + a.chunk[(bh * a.nch + ch) * a.C + l] + before + rank;
+        if ((unsigned)pos < (unsigned)a.N) a.perm[bh * a.N + pos] = t;
     }
+}
+
+static void launch_order(const OrdArgs& a, hipStream_t s) {
+    const int64_t BH = a.BH;
+    hipLaunchKernelGGL(ord_count_kernel, dim3((unsigned)(BH * a.nch)), dim3(kOrdChunk), 0, s, a);
+    hipLaunchKernelGGL(ord_scan_kernel, dim3((unsigned)((BH * a.C + 3) / 4)), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(ord_offsets_kernel, dim3((unsigned)BH), dim3(64), 0, s, a);
+    hipLaunchKernelGGL(ord_scatter_kernel, dim3((unsigned)(BH * a.nch)), dim3(kOrdChunk), 0, s, a);
 }
 
 // ---- row gather / scatter -------------------------------------------------------
@@ -379,10 +357,27 @@ __global__ __launch_bounds__(256) void cluster_scores_kernel(const float* cq, co
 
 using namespace vsa;
 
-extern "C" size_t vsa_kmeans_workspace_bytes(int B, int H, int C, int D) {
-    if (B <= 0 || H <= 0 || C <= 0 || D != kKmD) return 0;
-    const size_t rows = (size_t)B * H * C;
-    return ((rows * kKmD * 2 + 255) & ~(size_t)255) + ((rows * 4 + 255) & ~(size_t)255);
+static size_t km_al(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct KmPlan {
+    size_t off_bf, off_norm, off_perm, off_ofs, off_chunk, total;
+};
+
+static KmPlan km_plan(int64_t BH, int N, int C) {
+    KmPlan p;
+    const int64_t nch = (N + kOrdChunk - 1) / kOrdChunk;
+    p.off_bf = 0;
+    p.off_norm = km_al((size_t)BH * C * kKmD * 2);
+    p.off_perm = p.off_norm + km_al((size_t)BH * C * 4);
+    p.off_ofs = p.off_perm + km_al((size_t)BH * N * 4);
+    p.off_chunk = p.off_ofs + km_al((size_t)BH * (C + 1) * 4);
+    p.total = p.off_chunk + km_al((size_t)BH * nch * C * 4);
+    return p;
+}
+
+extern "C" size_t vsa_kmeans_workspace_bytes(int B, int H, int N, int C, int D) {
+    if (B <= 0 || H <= 0 || N <= 0 || C <= 0 || D != kKmD) return 0;
+    return km_plan((int64_t)B * H, N, C).total;
 }
 
 extern "C" int vsa_kmeans(const void* x, int B, int H, int N, int D, int dtype, int C, int iters, float* centroids,
@@ -392,32 +387,41 @@ extern "C" int vsa_kmeans(const void* x, int B, int H, int N, int D, int dtype, 
     if (!aligned16(x) || !aligned16(centroids)) return fail(VSA_ERR_INVALID, "%s: x and centroids must be 16-byte aligned", fn);
     if (B <= 0 || H <= 0 || N <= 0) return fail(VSA_ERR_INVALID, "%s: B, H, N must be positive", fn);
     if (C < 1 || C > N) return fail(VSA_ERR_INVALID, "%s: need 1 <= C <= N (C = %d, N = %d)", fn, C, N);
-    if (C > kKmMaxC) return fail(VSA_ERR_UNSUPPORTED, "%s: at most %d clusters", fn, kKmMaxC);
+    if (C > kOrdMaxC) return fail(VSA_ERR_UNSUPPORTED, "%s: at most %d clusters", fn, kOrdMaxC);
     if (iters < 1) return fail(VSA_ERR_INVALID, "%s: iters must be >= 1", fn);
     if (dtype != VSA_BF16 || D != kKmD) return fail(VSA_ERR_UNSUPPORTED, "%s: needs bf16 with D = %d", fn, kKmD);
     const int64_t BH = (int64_t)B * H;
-    if (BH * N >= (1ll << 31) || (int64_t)N * kKmD * 2 >= (1ll << 31)) return fail(VSA_ERR_INVALID, "%s: problem too large", fn);
-    const size_t need = vsa_kmeans_workspace_bytes(B, H, C, D);
-    if (!workspace || ws_bytes < need)
-        return fail(VSA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed (got %zu)", fn, need, ws_bytes);
+    const int64_t nch = (N + kOrdChunk - 1) / kOrdChunk;
+    if (BH * N >= (1ll << 31) || (int64_t)N * kKmD * 2 >= (1ll << 31) || BH * C >= (1ll << 31) ||
+        BH * nch * C >= (1ll << 31))
+        return fail(VSA_ERR_INVALID, "%s: problem too large", fn);
+    const KmPlan pl = km_plan(BH, N, C);
+    if (!workspace || ws_bytes < pl.total)
+        return fail(VSA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed (got %zu)", fn, pl.total, ws_bytes);
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
     KmArgs a{};
     a.x = static_cast<const uint16_t*>(x);
     a.cent = centroids;
-    a.cent_bf = static_cast<uint16_t*>(workspace);
-    a.cnorm = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) +
-                                       (((size_t)BH * C * kKmD * 2 + 255) & ~(size_t)255));
+    a.cent_bf = reinterpret_cast<uint16_t*>(ws + pl.off_bf);
+    a.cnorm = reinterpret_cast<float*>(ws + pl.off_norm);
     a.labels = labels;
     a.counts = counts;
     a.N = N; a.C = C; a.BH = (int32_t)BH;
+    OrdArgs o{};
+    o.labels = labels;
+    o.perm = reinterpret_cast<int32_t*>(ws + pl.off_perm);
+    o.offsets = reinterpret_cast<int32_t*>(ws + pl.off_ofs);
+    o.chunk = reinterpret_cast<int32_t*>(ws + pl.off_chunk);
+    o.N = N; o.C = C; o.BH = (int32_t)BH; o.nch = (int32_t)nch;
     hipStream_t s = as_stream(stream);
     hipLaunchKernelGGL(km_seed_kernel, dim3((unsigned)((BH * C + 3) / 4)), dim3(256), 0, s, a);
     int st = launch_status("vsa_kmeans (seeds)");
     if (st) return st;
     const int tiles = (N + 127) / 128;
-    const int groups = (C + kUpdClusters - 1) / kUpdClusters;
     for (int it = 0; it < iters; ++it) {
         hipLaunchKernelGGL(km_assign_kernel, dim3((unsigned)(BH * tiles)), dim3(256), 0, s, a, tiles);
-        hipLaunchKernelGGL(km_update_kernel, dim3((unsigned)(BH * groups)), dim3(kUpdWaves * 64), 0, s, a, groups);
+        launch_order(o, s);
+        hipLaunchKernelGGL(km_update_kernel, dim3((unsigned)(BH * C)), dim3(512), 0, s, a, o.perm, o.offsets);
         st = launch_status(fn);
         if (st) return st;
     }
@@ -430,10 +434,10 @@ extern "C" size_t vsa_cluster_order_workspace_bytes(int B, int H, int N, int C) 
     return (size_t)B * H * nch * C * 4;
 }
 
-extern "C" int vsa_cluster_order(const int32_t* labels, const int32_t* counts, int B, int H, int N, int C,
-                                 int32_t* perm, int32_t* offsets, void* workspace, size_t ws_bytes, void* stream) {
+extern "C" int vsa_cluster_order(const int32_t* labels, int B, int H, int N, int C, int32_t* perm, int32_t* offsets,
+                                 void* workspace, size_t ws_bytes, void* stream) {
     const char* fn = "vsa_cluster_order";
-    if (!labels || !counts || !perm || !offsets) return fail(VSA_ERR_INVALID, "%s: null tensor", fn);
+    if (!labels || !perm || !offsets) return fail(VSA_ERR_INVALID, "%s: null tensor", fn);
     if (B <= 0 || H <= 0 || N <= 0 || C <= 0) return fail(VSA_ERR_INVALID, "%s: B, H, N, C must be positive", fn);
     if (C > kOrdMaxC) return fail(VSA_ERR_UNSUPPORTED, "%s: at most %d clusters", fn, kOrdMaxC);
     const int64_t BH = (int64_t)B * H;
@@ -443,14 +447,10 @@ extern "C" int vsa_cluster_order(const int32_t* labels, const int32_t* counts, i
     if (!workspace || ws_bytes < need)
         return fail(VSA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed (got %zu)", fn, need, ws_bytes);
     OrdArgs a{};
-    a.labels = labels; a.counts = counts; a.perm = perm; a.offsets = offsets;
+    a.labels = labels; a.perm = perm; a.offsets = offsets;
     a.chunk = static_cast<int32_t*>(workspace);
     a.N = N; a.C = C; a.BH = (int32_t)BH; a.nch = (int32_t)nch;
-    hipStream_t s = as_stream(stream);
-    hipLaunchKernelGGL(ord_offsets_kernel, dim3((unsigned)BH), dim3(64), 0, s, a);
-    hipLaunchKernelGGL(ord_count_kernel, dim3((unsigned)(BH * nch)), dim3(kOrdChunk), 0, s, a);
-    hipLaunchKernelGGL(ord_scan_kernel, dim3((unsigned)((BH * C + 3) / 4)), dim3(256), 0, s, a);
-    hipLaunchKernelGGL(ord_scatter_kernel, dim3((unsigned)(BH * nch)), dim3(kOrdChunk), 0, s, a);
+    launch_order(a, as_stream(stream));
     return launch_status(fn);
 }
 

@@ -111,8 +111,8 @@ def semantic_layer(q, k, v, Cq, Ck, iters, top_p, k_max=None, scale=None, stats=
     """Returns o in natural order; `stats` receives the intermediate tensors."""
     cq, lq, nq = vsa_kmeans(q, Cq, iters)
     ck, lk, nk = vsa_kmeans(k, Ck, iters)
-    pq, oq = vsa_cluster_order(lq, nq)
-    pk, ok = vsa_cluster_order(lk, nk)
+    pq, oq = vsa_cluster_order(lq, Cq)
+    pk, ok = vsa_cluster_order(lk, Ck)
     qs = vsa_gather_rows(q, pq)
     ks = vsa_gather_rows(k, pk)
     vs = vsa_gather_rows(v, pk)

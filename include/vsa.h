@@ -309,31 +309,31 @@ int vsa_block_sparse_attn_bwd(const void* q, const void* k, const void* v, const
  * iterations. Seeds: the tokens at positions floor(c N / C). An iteration sends
  * every token to argmin_c ||m_c||^2 - 2 <x, m_c>, m_c the centroid rounded to
  * bf16 (fp32 accumulation, ties to the lower index), then replaces each
- * centroid by the mean of its members (fp32; an empty cluster keeps its
- * centroid). Deterministic: no floating-point atomics.
+ * centroid by the mean of its members (fp32, summed in a fixed order; an empty
+ * cluster keeps its centroid). Deterministic: no floating-point atomics.
  *   x          [B, H, N, D] bf16, D = 128 (otherwise VSA_ERR_UNSUPPORTED)
- *   C          1 <= C <= min(N, 4096)
+ *   C          1 <= C <= min(N, 1024)
  *   centroids  out, device fp32 [B, H, C, D]: the means of the final assignment
  *   labels     out, device int32 [B, H, N]: the final assignment
  *   counts     out, device int32 [B, H, C]: cluster sizes of the final assignment
- *   workspace  >= vsa_kmeans_workspace_bytes(B, H, C, D) bytes (bf16 centroids
- *              and their norms) */
-size_t vsa_kmeans_workspace_bytes(int B, int H, int C, int D);
+ *   workspace  >= vsa_kmeans_workspace_bytes(B, H, N, C, D) bytes (bf16
+ *              centroids and their norms, and each iteration's cluster order) */
+size_t vsa_kmeans_workspace_bytes(int B, int H, int N, int C, int D);
 int vsa_kmeans(const void* x, int B, int H, int N, int D, int dtype, int C, int iters, float* centroids,
                int32_t* labels, int32_t* counts, void* workspace, size_t ws_bytes, void* stream);
 
 /* Stable cluster-major order of every (b, h): tokens sorted by label, members of
  * a cluster in natural order. Integer work, bit-exact.
- *   labels   device int32 [B, H, N], entries in [0, C) (others are left out)
- *   counts   device int32 [B, H, C]: the label counts (as from vsa_kmeans)
+ *   labels   device int32 [B, H, N]; a label outside [0, C) leaves its token out
+ *            (positions from offsets[C] on are then not written)
  *   C        1 <= C <= 1024
  *   perm     out, device int32 [B, H, N]: perm[p] = token stored at position p
  *   offsets  out, device int32 [B, H, C + 1]: cluster c occupies positions
  *            [offsets[c], offsets[c + 1])
  *   workspace >= vsa_cluster_order_workspace_bytes(B, H, N, C) bytes */
 size_t vsa_cluster_order_workspace_bytes(int B, int H, int N, int C);
-int vsa_cluster_order(const int32_t* labels, const int32_t* counts, int B, int H, int N, int C,
-                      int32_t* perm, int32_t* offsets, void* workspace, size_t ws_bytes, void* stream);
+int vsa_cluster_order(const int32_t* labels, int B, int H, int N, int C, int32_t* perm, int32_t* offsets,
+                      void* workspace, size_t ws_bytes, void* stream);
 
 /* Row gather by a per-head index list (bit-exact data movement):
  *   inverse = 0: dst[b, h, r] = src[b, h, perm[b, h, r]]
@@ -368,10 +368,12 @@ int vsa_cluster_scores(const float* cq, const float* ck, const int32_t* k_counts
  *               uint8 [B, H, Cq, Ck] (Ck <= 4096), or kv_idx int32
  *               [B, H, Cq, max_kv] + kv_cnt [B, H, Cq] with distinct entries in
  *               [0, Ck), used in the order given (ascending = the mask form's order)
- *   workspace   >= vsa_varlen_attn_workspace_bytes(B, H, Cq) bytes
+ *   workspace   >= vsa_varlen_attn_workspace_bytes(B, H, N, Cq) bytes (chunk
+ *               table, kept-key counts and the launch order: the chunks with the
+ *               most kept keys start first)
  * Precision as vsa_block_sparse_attn_fwd. A query whose kept clusters hold no key
- * gets O = 0, LSE = -inf. */
-size_t vsa_varlen_attn_workspace_bytes(int B, int H, int Cq);
+ * gets O = 0, LSE = -inf. No floating-point atomics: results are bit-reproducible. */
+size_t vsa_varlen_attn_workspace_bytes(int B, int H, int N, int Cq);
 int vsa_varlen_sparse_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                                int B, int H, int N, int D, int dtype, const int32_t* q_off, int Cq,
                                const int32_t* k_off, int Ck, const vsa_blocks* blocks, float scale,

@@ -221,23 +221,24 @@ def test_backward_validation_and_workspace_size():
 def test_semantic_validation_and_workspace_sizes():
     L = V.lib()
     fake = ctypes.c_void_p(0x1000)
-    # k-means: bf16 centroids + norms, each rounded to 256 bytes
-    assert V.vsa_kmeans_workspace_bytes(1, 2, 100, 128) == 51200 + 1024
-    assert V.vsa_kmeans_workspace_bytes(1, 2, 100, 64) == 0
+    # k-means: bf16 centroids 51200, norms 800 -> 1024, order 8000 -> 8192,
+    # offsets 808 -> 1024, chunk table 2 x 4 x 100 x 4 = 3200 -> 3328
+    assert V.vsa_kmeans_workspace_bytes(1, 2, 1000, 100, 128) == 51200 + 1024 + 8192 + 1024 + 3328
+    assert V.vsa_kmeans_workspace_bytes(1, 2, 1000, 100, 64) == 0
     km = lambda **kw: L.vsa_kmeans(kw.get("x", fake), 1, 2, kw.get("N", 1000), kw.get("D", 128), kw.get("dtype", 0),
                                    kw.get("C", 100), kw.get("iters", 3), fake, fake, fake, fake,
                                    kw.get("ws", 1 << 20), None)
     assert km(x=None) == V.VSA_ERR_INVALID
     assert km(C=0) == V.VSA_ERR_INVALID
     assert km(C=1001) == V.VSA_ERR_INVALID                  # more clusters than tokens
-    assert km(N=10000, C=5000) == V.VSA_ERR_UNSUPPORTED
+    assert km(N=10000, C=2000) == V.VSA_ERR_UNSUPPORTED
     assert km(iters=0) == V.VSA_ERR_INVALID
     assert km(D=64) == V.VSA_ERR_UNSUPPORTED
     assert km(dtype=1) == V.VSA_ERR_UNSUPPORTED
     assert km(ws=100) == V.VSA_ERR_WORKSPACE
     # cluster order: chunk table of 4 chunks x 8 clusters per head
     assert V.vsa_cluster_order_workspace_bytes(1, 2, 1000, 8) == 2 * 4 * 8 * 4
-    co = lambda **kw: L.vsa_cluster_order(fake, fake, 1, 2, 1000, kw.get("C", 8), fake, fake, fake,
+    co = lambda **kw: L.vsa_cluster_order(fake, 1, 2, 1000, kw.get("C", 8), fake, fake, fake,
                                           kw.get("ws", 1 << 20), None)
     assert co(C=2000) == V.VSA_ERR_UNSUPPORTED
     assert co(ws=255) == V.VSA_ERR_WORKSPACE
@@ -252,14 +253,15 @@ def test_semantic_validation_and_workspace_sizes():
     assert sc(D=32) == V.VSA_ERR_UNSUPPORTED
     assert sc(scale=0.0) == V.VSA_ERR_INVALID
     # varlen attention
-    assert V.vsa_varlen_attn_workspace_bytes(1, 2, 7) == 2 * 8 * 4
+    # chunk table 2 x 8, kept keys 2 x 7, order 2 x (1000 // 128 + 7), count: each rounded to 256 bytes
+    assert V.vsa_varlen_attn_workspace_bytes(1, 2, 1000, 7) == 256 * 4
     blk = V.vsa_blocks()
     blk.mask = 0x1000
     va = lambda **kw: L.vsa_varlen_sparse_attn_fwd(
         fake, fake, fake, fake, None, 1, 2, 1000, kw.get("D", 128), 0, fake, 7, fake, kw.get("Ck", 9),
-        ctypes.byref(kw.get("blocks", blk)), 0.1, kw.get("ws", fake), kw.get("ws_bytes", 64), None)
+        ctypes.byref(kw.get("blocks", blk)), 0.1, kw.get("ws", fake), kw.get("ws_bytes", 1024), None)
     assert va(D=64) == V.VSA_ERR_UNSUPPORTED
     assert va(blocks=V.vsa_blocks()) == V.VSA_ERR_INVALID
     assert va(Ck=5000) == V.VSA_ERR_UNSUPPORTED               # mask row longer than a workgroup holds
     assert va(ws=None) == V.VSA_ERR_WORKSPACE
-    assert va(ws_bytes=63) == V.VSA_ERR_WORKSPACE
+    assert va(ws_bytes=1023) == V.VSA_ERR_WORKSPACE
