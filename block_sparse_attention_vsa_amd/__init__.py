@@ -21,6 +21,7 @@ VSA_OK, VSA_ERR_INVALID, VSA_ERR_UNSUPPORTED, VSA_ERR_LAUNCH, VSA_ERR_WORKSPACE 
 VSA_BF16, VSA_F32 = 0, 1
 VSA_PERM_FRAME_MAJOR, VSA_PERM_CUBE4 = 0, 1
 VSA_PATTERN_SPATIAL, VSA_PATTERN_TEMPORAL = 0, 1
+VSA_FP8_ROWS, VSA_FP8_VT = 0, 1
 
 
 class vsa_grid(ctypes.Structure):
@@ -73,6 +74,9 @@ _SIGNATURES = {
     "vsa_varlen_attn_workspace_bytes": (_SZ, [_I, _I, _I, _I]),
     "vsa_varlen_sparse_attn_fwd": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _I, _P, _I,
                                         ctypes.POINTER(vsa_blocks), _F, _P, _SZ, _P]),
+    "vsa_fp8_quantize": (_I, [_P, _I, _I, _I, _I, _I, _I, _P, _P, _P]),
+    "vsa_block_sparse_attn_fwd_fp8": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P,
+                                           ctypes.POINTER(vsa_blocks), _F, _P]),
     "vsa_check_block_list_host": (_I, [_P, _P, _I64, _I, _I]),
 }
 
@@ -561,6 +565,45 @@ def vsa_varlen_sparse_attn_fwd(q, k, v, q_off, k_off, mask=None, kv_idx=None, kv
                                             _dtype_code(q), _ptr(q_off), Cq, _ptr(k_off), Ck, ctypes.byref(blocks),
                                             scale, _ptr(workspace), workspace.numel(), _stream(q.device)),
            "vsa_varlen_sparse_attn_fwd")
+    return (out, lse) if return_lse else out
+
+
+def vsa_fp8_quantize(x, kind: int, out=None, scales=None):
+    """e4m3 codes and scales of x [B, H, N, D] (bf16): kind VSA_FP8_ROWS gives
+    ([B, H, N, D], [B, H, ceil(N/64)]), VSA_FP8_VT ([B, H, ceil(N/64), D, 64], [B, H, D])."""
+    torch = _torch()
+    _need(x, "x", ndim=4)
+    B, H, N, D = x.shape
+    nt = -(-N // 64)
+    if out is None:
+        shape = (B, H, N, D) if kind == VSA_FP8_ROWS else (B, H, nt, D, 64)
+        out = torch.empty(shape, dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((B, H, nt) if kind == VSA_FP8_ROWS else (B, H, D), dtype=torch.float32, device=x.device)
+    _check(lib().vsa_fp8_quantize(_ptr(x), B, H, N, D, _dtype_code(x), kind, _ptr(out), _ptr(scales),
+                                  _stream(x.device)), "vsa_fp8_quantize")
+    return out, scales
+
+
+def vsa_block_sparse_attn_fwd_fp8(q8, k8, vt8, q_scale, k_scale, v_scale, bs: int, mask=None, kv_idx=None,
+                                  kv_cnt=None, blk_len=None, scale=None, return_lse=False, out=None, lse=None):
+    torch = _torch()
+    _need(q8, "q8", torch.uint8, 4)
+    _need(k8, "k8", torch.uint8, 4)
+    _need(vt8, "vt8", torch.uint8, 5)
+    B, H, N, D = q8.shape
+    scale = default_scale(D) if scale is None else scale
+    if out is None:
+        out = torch.empty((B, H, N, D), dtype=torch.bfloat16, device=q8.device)
+    if return_lse and lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q8.device)
+    if blk_len is not None:
+        _need(blk_len, "blk_len", torch.int32, 1)
+    blocks = _blocks_arg(q8, bs, mask, kv_idx, kv_cnt)
+    _check(lib().vsa_block_sparse_attn_fwd_fp8(_ptr(q8), _ptr(k8), _ptr(vt8), _ptr(q_scale), _ptr(k_scale),
+                                               _ptr(v_scale), _ptr(out), _ptr(lse), B, H, N, D, bs, _ptr(blk_len),
+                                               ctypes.byref(blocks), scale, _stream(q8.device)),
+           "vsa_block_sparse_attn_fwd_fp8")
     return (out, lse) if return_lse else out
 
 

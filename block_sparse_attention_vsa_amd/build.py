@@ -20,7 +20,7 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libvsa.so")
 
 SOURCES = ["status.hip", "pattern.hip", "permute.hip", "attn_fwd.hip", "attn_bwd.hip", "scores.hip", "select.hip",
-           "profile.hip", "semantic.hip", "attn_varlen.hip"]
+           "profile.hip", "semantic.hip", "attn_varlen.hip", "attn_fp8.hip"]
 
 ARCH = "gfx950"
 FLAGS = [

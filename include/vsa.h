@@ -66,6 +66,13 @@ enum vsa_pattern {
     VSA_PATTERN_TEMPORAL = 1  /* |s_q - s_k| <= w, s = y*W + x, in frame-major order */
 };
 
+/* FP8 layouts (vsa_fp8_quantize). */
+enum vsa_fp8_kind {
+    VSA_FP8_ROWS = 0,         /* [B, H, N, D] codes, one scale per (b, h, 64 rows)          */
+    VSA_FP8_VT = 1            /* [B, H, ceil(N/64), D, 64] transposed 64-key tiles, one
+                                 scale per (b, h, channel)                                 */
+};
+
 typedef struct { int32_t T, Hh, W; } vsa_grid;
 
 /* Block sets for vsa_block_sparse_attn_fwd: exactly one of `mask` or
@@ -378,6 +385,38 @@ int vsa_varlen_sparse_attn_fwd(const void* q, const void* k, const void* v, void
                                int B, int H, int N, int D, int dtype, const int32_t* q_off, int Cq,
                                const int32_t* k_off, int Ck, const vsa_blocks* blocks, float scale,
                                void* workspace, size_t ws_bytes, void* stream);
+
+/* ---- FP8 attention ----------------------------------------------------------
+ * Sparse Video-Gen page, "Key results": the attention runs faster still in FP8.
+ * Format OCP E4M3 (bias 7, largest finite 448, round to nearest even). */
+
+/* Quantises a bf16 tensor to e4m3: code = e4m3(clamp(x * (448 / amax), +-448)),
+ * both products in fp32, scale = amax / 448 (a zero block: scale 0, codes 0).
+ *   x       [B, H, N, D] bf16, D = 128 (otherwise VSA_ERR_UNSUPPORTED)
+ *   kind    VSA_FP8_ROWS (for Q and K): out [B, H, N, D], scales fp32
+ *           [B, H, ceil(N / 64)], amax over each block of 64 rows and all channels;
+ *           VSA_FP8_VT (for V): out [B, H, ceil(N / 64), D, 64] with key
+ *           k = 32 st + 8 g + 4 h + e (st, h in {0, 1}; g, e < 4) of a tile at
+ *           column 32 h + 16 st + 4 g + e and keys past N zero, scales fp32
+ *           [B, H, D], amax per channel over all N rows
+ * No workspace (VSA_FP8_VT uses `scales` for the amax bits until its last step). */
+int vsa_fp8_quantize(const void* x, int B, int H, int N, int D, int dtype, int kind, uint8_t* out,
+                     float* scales, void* stream);
+
+/* Block-sparse attention on e4m3 inputs: softmax attention of the dequantised
+ * values code * scale (same block rule as vsa_block_sparse_attn_fwd), on the
+ * gfx950 e4m3 MFMA. S in fp32 from exact code products; P = exp(S - m) in fp32
+ * is rounded to e4m3 for P V (the row sum uses the fp32 P); O rounded to bf16.
+ *   q8, k8        codes from vsa_fp8_quantize(VSA_FP8_ROWS), with their scales
+ *   vt8, v_scale  codes and scales from vsa_fp8_quantize(VSA_FP8_VT)
+ *   o             out [B, H, N, D] bf16; lse optional out fp32 [B, H, N] (natural log)
+ *   D = 128, bs = 128 (otherwise VSA_ERR_UNSUPPORTED); blk_len, blocks, scale as for
+ *   vsa_block_sparse_attn_fwd. No workspace. */
+int vsa_block_sparse_attn_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* vt8,
+                                  const float* q_scale, const float* k_scale, const float* v_scale,
+                                  void* o, float* lse, int B, int H, int N, int D, int bs,
+                                  const int32_t* blk_len, const vsa_blocks* blocks, float scale,
+                                  void* stream);
 
 /* Validates a block list held in HOST memory: every kv_cnt in [0, max_kv], the
  * first kv_cnt entries of each row strictly ascending and inside [0, nkb).

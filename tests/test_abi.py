@@ -265,3 +265,24 @@ def test_semantic_validation_and_workspace_sizes():
     assert va(Ck=5000) == V.VSA_ERR_UNSUPPORTED               # mask row longer than a workgroup holds
     assert va(ws=None) == V.VSA_ERR_WORKSPACE
     assert va(ws_bytes=1023) == V.VSA_ERR_WORKSPACE
+
+
+def test_fp8_validation():
+    L = V.lib()
+    fake = ctypes.c_void_p(0x1000)
+    qz = lambda **kw: L.vsa_fp8_quantize(kw.get("x", fake), 1, 2, 100, kw.get("D", 128), kw.get("dtype", 0),
+                                         kw.get("kind", 0), fake, fake, None)
+    assert qz(x=None) == V.VSA_ERR_INVALID
+    assert qz(D=64) == V.VSA_ERR_UNSUPPORTED
+    assert qz(dtype=1) == V.VSA_ERR_UNSUPPORTED
+    assert qz(kind=5) == V.VSA_ERR_INVALID
+    blk = V.vsa_blocks()
+    blk.mask = 0x1000
+    at = lambda **kw: L.vsa_block_sparse_attn_fwd_fp8(
+        fake, fake, fake, fake, fake, kw.get("vs", fake), fake, None, 1, 2, 1000, kw.get("D", 128), kw.get("bs", 128),
+        None, ctypes.byref(kw.get("blocks", blk)), kw.get("scale", 0.1), None)
+    assert at(vs=None) == V.VSA_ERR_INVALID
+    assert at(D=64) == V.VSA_ERR_UNSUPPORTED
+    assert at(bs=64) == V.VSA_ERR_UNSUPPORTED
+    assert at(scale=-1.0) == V.VSA_ERR_INVALID
+    assert at(blocks=V.vsa_blocks()) == V.VSA_ERR_INVALID

@@ -1,0 +1,122 @@
+"""GPU parity of the FP8 (e4m3) path against the oracle: the quantisers bit for
+bit (codes and scales), attention whose probabilities are exact in e4m3 (one or
+two equal maxima per row) to the bf16 output precision, random problems within
+the error that rounding P to e4m3 can cause, and sampled rows at the Wan shape."""
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_attention_vsa_amd as V
+from oracle import fp8 as OF
+from oracle import masks as OM
+from tests.gpu_util import announce, assert_lse_close, dev, dev_i32, dev_u8, host
+from workloads import WAN480, make_qkv, sample_rows
+
+pytestmark = pytest.mark.gpu
+
+# Rounding P to e4m3 (3 mantissa bits) before P V: emulating it against the fp64
+# attention on the dequantised inputs gives a largest error of 0.11 and a mean
+# error of 0.05 of the output's largest / mean magnitude (unit-scale inputs;
+# 0.03 / 0.013 with 4x logits). The bars leave about 2.5x room; a dropped tile,
+# a wrong scale or a mismatched key order moves the mean by far more.
+FP8_MAX_REL = 0.3
+FP8_MEAN_REL = 0.13
+
+
+def bf16_values(x):
+    return torch.from_numpy(np.asarray(x, np.float32)).to(torch.bfloat16).float().numpy().astype(np.float64)
+
+
+def quantised(q, k, v):
+    qd, kd, vd = dev(q), dev(k), dev(v)
+    q8, qs = V.vsa_fp8_quantize(qd, V.VSA_FP8_ROWS)
+    k8, ks = V.vsa_fp8_quantize(kd, V.VSA_FP8_ROWS)
+    vt, vs = V.vsa_fp8_quantize(vd, V.VSA_FP8_VT)
+    return q8, k8, vt, qs, ks, vs                         # the binding's argument order
+
+
+@pytest.mark.parametrize("N,amp", [(1000, 1.0), (777, 30.0), (64, 1.0), (1, 1.0), (200, 1e-3)])
+def test_quantise_bit_exact(N, amp):
+    announce(f"fp8 quantise N={N} amp={amp}")
+    g = np.random.default_rng(N)
+    x = bf16_values(amp * g.standard_normal((1, 2, N, 128)) * np.exp(g.standard_normal((1, 2, N, 1))))
+    if N >= 128:
+        x[0, 1, 64:128] = 0.0                                  # a zero block
+    xd = dev(x)
+    c, s = (host(t) for t in V.vsa_fp8_quantize(xd, V.VSA_FP8_ROWS))
+    rc, rs = OF.quantise_rows(x)
+    assert (c == rc).all() and (s == rs).all()
+    t, vs = (host(u) for u in V.vsa_fp8_quantize(xd, V.VSA_FP8_VT))
+    vc, rvs = OF.quantise_channels(x)
+    assert (vs == rvs).all()
+    assert (t == OF.vt_tiles(vc)).all()
+
+
+@pytest.mark.parametrize("keep_both", [True, False])
+def test_fp8_attention_exact_probabilities(keep_both):
+    """Key j is 448 e_(j mod 128), query i is 448 e_pi(i): every row has one or two
+    equal maximal scores (17,700 above the rest), so P is exactly 1 at those keys
+    and 0 elsewhere, and O is the mean of one or two dequantised V rows."""
+    announce(f"fp8 attention exact P keep_both={keep_both}")
+    g = np.random.default_rng(7)
+    N, H = 256, 2
+    k = np.zeros((1, H, N, 128))
+    k[0, :, np.arange(N), np.arange(N) % 128] = 448.0
+    q = np.zeros((1, H, N, 128))
+    for h in range(H):
+        q[0, h, np.arange(N), g.permutation(N) % 128] = 448.0
+    v = bf16_values(g.standard_normal((1, H, N, 128)))
+    mask = np.ones((1, H, 2, 2), np.uint8)
+    if not keep_both:
+        mask[0, 0, 0, 1] = 0
+        mask[0, 1, 1, 0] = 0
+    o, lse = V.vsa_block_sparse_attn_fwd_fp8(*quantised(q, k, v), 128, mask=dev_u8(mask), return_lse=True)
+    ro, rl, _ = OF.attention_fp8(q, k, v, mask, 128)
+    np.testing.assert_allclose(host(o), ro, rtol=8e-3, atol=1e-4)
+    assert_lse_close(host(lse), rl, "exact P", tol=1e-3 * np.abs(rl).max())
+
+
+@pytest.mark.parametrize("N,H,amp", [(1000, 3, 1.0), (777, 2, 1.0), (640, 2, 4.0), (128, 1, 1.0), (65, 1, 1.0)])
+def test_fp8_attention_random_masks(N, H, amp):
+    announce(f"fp8 attention N={N} H={H} amp={amp}")
+    g = np.random.default_rng(N + H)
+    q, k = (bf16_values(amp * g.standard_normal((1, H, N, 128))) for _ in range(2))
+    v = bf16_values(g.standard_normal((1, H, N, 128)))
+    nb = -(-N // 128)
+    mask = (g.random((1, H, nb, nb)) < 0.4).astype(np.uint8)
+    mask[..., np.arange(nb), np.arange(nb)] = 1
+    ins = quantised(q, k, v)
+    o, lse = V.vsa_block_sparse_attn_fwd_fp8(*ins, 128, mask=dev_u8(mask), return_lse=True)
+    ro, rl, _ = OF.attention_fp8(q, k, v, mask, 128)
+    go = host(o)
+    d = np.abs(go - ro)
+    assert np.isfinite(go).all()
+    assert d.max() <= FP8_MAX_REL * np.abs(ro).max(), d.max()
+    assert d.mean() <= FP8_MEAN_REL * np.abs(ro).mean(), d.mean()
+    # the row sums use the unrounded P: the LSE is exact up to fp32
+    assert_lse_close(host(lse), rl, f"fp8 N={N}", tol=2e-3 * max(1.0, amp ** 2))
+    idx, cnt = OM.mask_to_list(mask)
+    o2 = V.vsa_block_sparse_attn_fwd_fp8(*ins, 128, kv_idx=dev_i32(idx), kv_cnt=dev_i32(cnt))
+    assert torch.equal(o, o2)
+    o3 = V.vsa_block_sparse_attn_fwd_fp8(*ins, 128, mask=dev_u8(mask))
+    assert torch.equal(o, o3)
+
+
+def test_fp8_attention_wan_shape_sampled():
+    """Wan 480p shape (2 heads), spatial w = 1 block mask: sampled rows."""
+    w = WAN480
+    announce("fp8 attention wan shape")
+    q, k, v = make_qkv(w, H=2)
+    mask = OM.pattern_mask(w.grid, w.bs, "spatial", 1)[None, None].repeat(2, axis=1)
+    o, lse = V.vsa_block_sparse_attn_fwd_fp8(*quantised(q, k, v), 128, mask=dev_u8(mask), return_lse=True)
+    rows = sample_rows(w.N, 128, 512, 5)
+    qc, qs = OF.quantise_rows(q)
+    kc, ks = OF.quantise_rows(k)
+    vc, vs = OF.quantise_channels(v)
+    from oracle import attention as OA
+    ro, rl = OA.block_sparse_attention(OF.dequantise_rows(qc, qs), OF.dequantise_rows(kc, ks),
+                                       OF.dequantise_channels(vc, vs), mask, 128, rows=rows)
+    go = host(o)[:, :, rows]
+    d = np.abs(go - ro)
+    assert d.max() <= FP8_MAX_REL * np.abs(ro).max() and d.mean() <= FP8_MEAN_REL * np.abs(ro).mean()
+    assert_lse_close(host(lse)[:, :, rows], rl, "fp8 wan", tol=2e-3)
