@@ -33,6 +33,7 @@ sys.path.insert(0, ROOT)
 from workloads import WAN480, WAN480_CUBE, WAN480_SEMANTIC, LONG126, make_qkv, profile_rows  # noqa: E402
 
 PEAK_BF16_TFLOPS = 2516.6       # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5033.2        # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0
 
 
@@ -449,6 +450,35 @@ def extra_layers(torch, V, PL, T):
                                                    kept_flops_from_lists(bi, bc, w.N, w.bs, 128), mask=mask)
     res["attn_bwd_spatial_wan480"]["what"] = ("vsa_block_sparse_attn_bwd, [1,12,32760,128] bf16, bs 128, spatial "
                                               "w=1 block mask on all heads")
+
+    # FP8 (e4m3) attention under the same mask: quantisation of Q, K, V, then the
+    # fp8 kernel, against the bf16 kernel on the same inputs
+    fl_sp = kept_flops_from_lists(bi, bc, w.N, w.bs, 128)
+    times = {}
+    for rep in range(4):
+        e = [T.ev()]
+        q8, qs = V.vsa_fp8_quantize(q, V.VSA_FP8_ROWS)
+        k8, ks = V.vsa_fp8_quantize(k, V.VSA_FP8_ROWS)
+        vt8, vs8 = V.vsa_fp8_quantize(v, V.VSA_FP8_VT)
+        e.append(T.ev())
+        o8 = V.vsa_block_sparse_attn_fwd_fp8(q8, k8, vt8, qs, ks, vs8, w.bs, mask=mask)
+        e.append(T.ev())
+        ob = V.vsa_block_sparse_attn_fwd(q, k, v, w.bs, mask=mask)
+        e.append(T.ev())
+        torch.cuda.synchronize()
+        if rep:
+            for key, i in (("quantise_qkv", 0), ("fp8_attention", 1), ("bf16_attention", 2)):
+                times.setdefault(key, []).append(e[i].elapsed_time(e[i + 1]))
+    ms = {k_: round(float(np.mean(v_)), 4) for k_, v_ in times.items()}
+    rel = float(((o8.float() - ob.float()).abs().mean() / ob.float().abs().mean()).item())
+    res["fp8_spatial_wan480"] = {"ms": ms, "kept_flops": fl_sp,
+                                 "fp8_attn_tflops": round(fl_sp / (ms["fp8_attention"] * 1e-3) / 1e12, 2),
+                                 "bf16_attn_tflops": round(fl_sp / (ms["bf16_attention"] * 1e-3) / 1e12, 2),
+                                 "pct_fp8_mfma_peak": round(100 * fl_sp / (ms["fp8_attention"] * 1e-3) / 1e12
+                                                            / PEAK_FP8_TFLOPS, 2),
+                                 "speedup_vs_bf16": round(ms["bf16_attention"] / ms["fp8_attention"], 3),
+                                 "mean_rel_diff_vs_bf16": round(rel, 4)}
+    del q8, k8, vt8, o8, ob
     del q, k, v, m, mask, bi, bc
     torch.cuda.empty_cache()
 
