@@ -30,7 +30,8 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-from workloads import WAN480, WAN480_CUBE, WAN480_SEMANTIC, LONG126, make_qkv, profile_rows  # noqa: E402
+from workloads import (WAN480, WAN480_CUBE, WAN480_SEMANTIC, LONG126, HUNYUAN720, make_qkv,  # noqa: E402
+                       profile_rows)
 
 PEAK_BF16_TFLOPS = 2516.6       # MI355X dense bf16 MFMA
 PEAK_FP8_TFLOPS = 5033.2        # MI355X dense fp8 MFMA
@@ -319,6 +320,11 @@ def main():
     perm_gbs = 2 * q.numel() * q.element_size() / (perm_ms * 1e-3) / 1e9
     del pdst
 
+    # the step's attention launch alone, warm and cold, and what the box reaches on plain work
+    kstats = launch_stats(torch, T, lambda: V.vsa_block_sparse_attn_fwd_chosen(q, k, v, grid, bs, cand, [0, 1], ch),
+                          flops)
+    achievable = achievable_peaks(torch, T)
+
     extra = {}
     if not args.no_extra:
         extra = extra_layers(torch, V, PL, T)
@@ -331,7 +337,8 @@ def main():
     roofline = {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
                 "kernel": kname, "per_launch_flops": flops,
-                "avg_launch_ms": round(attn_ms, 4)}
+                "avg_launch_ms": round(attn_ms, 4),
+                "frac_of_achievable": round(attn_tflops / achievable["bf16_gemm_tflops"], 4)}
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -360,14 +367,93 @@ def main():
         "speedup_vs_dense_step": round(dense_ms / ms_step, 2),
         "dense_ms": {"ours_all_blocks": round(dense_ours, 3), "torch_sdpa": None if dense_sdpa is None else round(dense_sdpa, 3)},
         "components_ms": comp,
+        "attention_launch_stats": kstats,
+        "achievable_peaks": achievable,
+        "environment": environment(torch),
         "permute_standalone": {"ms": round(perm_ms, 4), "GBps": round(perm_gbs, 1),
                                "frac_of_hbm_peak": round(perm_gbs / 8000.0, 3),
+                               "frac_of_copy": round(perm_gbs / achievable["copy_GBps"], 3),
                                "what": "vsa_permute frame-major, all 12 heads of one [1,12,32760,128] bf16 tensor"},
         "extra_layers": extra,
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+
+
+def launch_stats(torch, T, fn, flops, runs=50, warm=5, flush_bytes=1 << 30):
+    """One kernel launch timed alone: `runs` launches after `warm`, each bracketed
+    by HIP events on the current stream; warm (back to back) and cold (a 1 GiB
+    buffer written before each launch, which evicts L2 and the 256 MB MALL).
+    Median, p10, p90 in ms and TFLOP/s at the median."""
+    dev = torch.device("cuda:0")
+    buf = torch.empty((flush_bytes,), dtype=torch.uint8, device=dev)
+    out = {}
+    for mode in ("warm", "cold"):
+        for _ in range(warm):
+            fn()
+        torch.cuda.synchronize()
+        ts = []
+        for i in range(runs):
+            if mode == "cold":
+                buf.fill_(i & 255)
+            e0 = T.ev()
+            fn()
+            e1 = T.ev()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        ts = np.array(ts)
+        med = float(np.median(ts))
+        out[mode] = {"median_ms": round(med, 4), "p10_ms": round(float(np.percentile(ts, 10)), 4),
+                     "p90_ms": round(float(np.percentile(ts, 90)), 4),
+                     "tflops_at_median": round(flops / (med * 1e-3) / 1e12, 2)}
+    del buf
+    return out
+
+
+def achievable_peaks(torch, T):
+    """What this machine reaches on plain work: a bf16 GEMM (torch / hipBLASLt,
+    8192^3) and a 1 GiB device-to-device copy."""
+    dev = torch.device("cuda:0")
+    n = 8192
+    a = torch.randn((n, n), device=dev, dtype=torch.bfloat16)
+    b = torch.randn((n, n), device=dev, dtype=torch.bfloat16)
+    for _ in range(3):
+        torch.matmul(a, b)
+    torch.cuda.synchronize()
+    e0 = T.ev()
+    for _ in range(10):
+        torch.matmul(a, b)
+    e1 = T.ev()
+    torch.cuda.synchronize()
+    gemm = 2.0 * n ** 3 / (e0.elapsed_time(e1) / 10 * 1e-3) / 1e12
+    del a, b
+    src = torch.empty((1 << 30,), dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0 = T.ev()
+    for _ in range(10):
+        dst.copy_(src)
+    e1 = T.ev()
+    torch.cuda.synchronize()
+    copy = 2.0 * (1 << 30) / (e0.elapsed_time(e1) / 10 * 1e-3) / 1e9
+    del src, dst
+    return {"bf16_gemm_tflops": round(gemm, 1), "copy_GBps": round(copy, 1),
+            "what": "torch.matmul bf16 8192x8192x8192; 1 GiB device copy (read + write counted)"}
+
+
+def environment(torch):
+    env = {"torch": torch.__version__, "hip": getattr(torch.version, "hip", None),
+           "device": torch.cuda.get_device_name(0)}
+    try:
+        import subprocess
+        r = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=30)
+        env["clocks"] = [ln.strip() for ln in r.stdout.splitlines() if "clk" in ln.lower()][:6]
+    except Exception as ex:   # report, do not hide
+        env["clocks"] = f"rocm-smi unavailable: {ex}"
+    return env
 
 
 def time_backward(torch, V, T, q, k, v, bs, fwd_flops, reps=4, **blocks):
@@ -480,6 +566,46 @@ def extra_layers(torch, V, PL, T):
                                  "mean_rel_diff_vs_bf16": round(rel, 4)}
     del q8, k8, vt8, o8, ob
     del q, k, v, m, mask, bi, bc
+    torch.cuda.empty_cache()
+
+    # HunyuanVideo 720p layer (24 heads, 118,800 tokens): planted 12/12 split, even
+    # heads spatial w=2, odd heads temporal w=276 in frame-major order (folded into
+    # the attention's loads and stores); and the a3 permutation of one tensor with
+    # all 24 heads moved
+    w = HUNYUAN720
+    q, k, v = (torch.from_numpy(x).to(torch.bfloat16).to(dev) for x in make_qkv(w))
+    sel = [h % 2 for h in range(w.H)]
+    cand = PL.svg_masks(w.grid, w.bs, w.extra["w_spatial"], w.extra["w_temporal"], dev)
+    idx, cnt = V.vsa_mask_to_list(cand, head_mask_idx=sel, B=1)
+    fl = kept_flops_from_lists(idx, cnt, w.N, w.bs, 128)
+    ts = []
+    for rep in range(4):
+        e0 = T.ev()
+        o = V.vsa_block_sparse_attn_fwd_permuted(q, k, v, w.grid, w.bs, head_fm=sel, kv_idx=idx, kv_cnt=cnt)
+        e1 = T.ev()
+        torch.cuda.synchronize()
+        if rep:
+            ts.append(e0.elapsed_time(e1))
+    t_att = float(np.mean(ts))
+    pdst = torch.empty_like(q)
+    for _ in range(2):
+        V.vsa_permute(q, w.grid, V.VSA_PERM_FRAME_MAJOR, False, [1] * w.H, out=pdst)
+    torch.cuda.synchronize()
+    e0 = T.ev()
+    for _ in range(10):
+        V.vsa_permute(q, w.grid, V.VSA_PERM_FRAME_MAJOR, False, [1] * w.H, out=pdst)
+    e1 = T.ev()
+    torch.cuda.synchronize()
+    p_ms = e0.elapsed_time(e1) / 10
+    p_gbs = 2 * q.numel() * q.element_size() / (p_ms * 1e-3) / 1e9
+    res["svg_hunyuan720"] = {"attention_ms": round(t_att, 3), "kept_flops": fl,
+                             "attn_tflops": round(fl / (t_att * 1e-3) / 1e12, 2),
+                             "pct_mfma_peak": round(100 * fl / (t_att * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+                             "permute_all_heads": {"ms": round(p_ms, 4), "GBps": round(p_gbs, 1),
+                                                   "frac_of_hbm_peak": round(p_gbs / PEAK_HBM_GBS, 3),
+                                                   "bytes": 2 * q.numel() * q.element_size()},
+                             "what": "vsa_block_sparse_attn_fwd_permuted, [1,24,118800,128] bf16, bs 128"}
+    del q, k, v, o, pdst, cand, idx, cnt
     torch.cuda.empty_cache()
 
     w = WAN480_CUBE
