@@ -10,8 +10,9 @@ import block_sparse_attention_vsa_amd as V
 from oracle import attention as OA
 from oracle import layout as OL
 from oracle import masks as OM
+from oracle import pipeline as OP
 from tests.gpu_util import announce, assert_close_bf16, assert_lse_close, dev, dev_i32, dev_u8, host
-from workloads import WAN480, make_qkv, sample_rows
+from workloads import HUNYUAN720, WAN480, make_qkv, sample_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -152,3 +153,24 @@ def test_chosen_wan_full_shape_matches_list_path():
     idx, cnt = V.vsa_mask_to_list(cand, head_mask_idx=sel, B=1)
     o_l = V.vsa_block_sparse_attn_fwd_permuted(qd, kd, vd, w.grid, w.bs, head_fm=sel, kv_idx=idx, kv_cnt=cnt)
     assert torch.equal(o_c, o_l)
+
+
+def test_fused_hunyuan_full_shape_sampled():
+    """HunyuanVideo 720p in the launch configuration the benchmark times: 24 heads,
+    118,800 tokens, even heads spatial w=2, odd heads temporal w=276 through the
+    frame-major map folded into the kernel; sampled rows of two spatial and two
+    temporal heads against the oracle's pipeline."""
+    w = HUNYUAN720
+    announce("fused attn hunyuan full shape")
+    q, k, v = make_qkv(w)
+    head_fm = [h % 2 for h in range(w.H)]
+    cand = np.stack([OM.pattern_mask(w.grid, w.bs, "spatial", w.extra["w_spatial"]),
+                     OM.pattern_mask(w.grid, w.bs, "temporal", w.extra["w_temporal"])])
+    idx, cnt = V.vsa_mask_to_list(dev_u8(cand), head_mask_idx=head_fm, B=1)
+    o = V.vsa_block_sparse_attn_fwd_permuted(dev(q), dev(k), dev(v), w.grid, w.bs, head_fm=head_fm, kv_idx=idx,
+                                             kv_cnt=cnt)
+    heads = [0, 1, 22, 23]
+    rows = sample_rows(w.N, w.bs, 128, 23)
+    ro, _ = OP.svg_pipeline(q[:, heads], k[:, heads], v[:, heads], w.grid, w.bs, [[head_fm[h] for h in heads]],
+                            w.extra["w_spatial"], w.extra["w_temporal"], rows=rows)
+    assert_close_bf16(host(o[:, heads])[:, :, rows], ro, "fused hunyuan")
