@@ -215,7 +215,7 @@ def main():
         cpu_leg(args)
         return
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); the per-head work "
+        print(f"bench.py: runs on one GPU only (asked for --gpus {args.gpus}); the per-head work "
               f"shards across GPUs with no exchange, which is not exercised here.", file=sys.stderr)
         sys.exit(2)
 
