@@ -448,8 +448,12 @@ def environment(torch):
     env = {"torch": torch.__version__, "hip": getattr(torch.version, "hip", None),
            "device": torch.cuda.get_device_name(0)}
     try:
+        import shutil
         import subprocess
-        r = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=30)
+        # run the tool's script with this interpreter: its "#!/usr/bin/env" line
+        # would otherwise have env replace itself with python inside the child
+        smi = os.path.realpath(shutil.which("rocm-smi") or "/opt/rocm/bin/rocm-smi")
+        r = subprocess.run([sys.executable, smi, "--showclocks"], capture_output=True, text=True, timeout=30)
         env["clocks"] = [ln.strip() for ln in r.stdout.splitlines() if "clk" in ln.lower()][:6]
     except Exception as ex:   # report, do not hide
         env["clocks"] = f"rocm-smi unavailable: {ex}"

@@ -365,7 +365,7 @@ __global__ __launch_bounds__(BS * 4) __attribute__((amdgpu_waves_per_eu(2))) voi
                 for (int st = 0; st < NST; ++st) dp[st] = tile_rows_mma_at(ot, st, kv, ad);   // dP = dO V^T
             }
         }
-        __syncthreads();                              // P visible to the dS waves
+        lds_barrier();                                // P visible to the dS waves; the next stage's copy runs on
         // phase 2: dV^T += dO^T P (P wave) | dS, dK^T += Q^T dS (dS wave)
         if (!active) return;
         if (!ds_wave) {

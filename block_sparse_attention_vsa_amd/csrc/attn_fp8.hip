@@ -254,7 +254,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
         int kb;
         const int vs = sub_valid(i, kb);
         if (!wave_active || vs == 0) return;
-        const float sk = a.k_scale[(int64_t)bh * a.ntile + (kb * BS + (i % SUB) * KT) / KT];
+        // the block index is uniform: a scalar load keeps the key scale off the
+        // vector-memory counter, so reading it does not wait for the next stage's copy
+        const int kt_idx = (__builtin_amdgcn_readfirstlane(kb) * BS + (i % SUB) * KT) / KT;
+        const float sk = ((const __attribute__((address_space(4))) float*)a.k_scale)[(int64_t)bh * a.ntile + kt_idx];
         const float mul = sq * sk * a.scale_log2;
         f32x16 s[NST];
 #pragma unroll

@@ -276,6 +276,7 @@ __global__ __launch_bounds__(BS * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
         return v < 0 ? 0 : (v > KT ? KT : v);
     };
     const SubTileDma<WAVES, kVSwz4, KT> dma(lane, w);
+    const SubVtAddr vad(lane);
     const int head_bytes = a.N * D * 2;
     // natural rows / rows through the frame-major map; the main loop below is
     // instantiated once per form, so a natural head runs no gather code
@@ -358,7 +359,7 @@ __global__ __launch_bounds__(BS * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
             for (int st = 0; st < NST; ++st)
 #pragma unroll
                 for (int g = 0; g < 2; ++g)
-                    o_acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sub_vt_operand(vt, dt, st, g, lane),
+                    o_acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sub_vt_operand(vt, dt, st, g, vad),
                                                                         pf[st][g], o_acc[dt], 0, 0, 0);
     };
 

@@ -247,25 +247,34 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
     const int n_sub = (L + KT - 1) / KT;
 
     const SubTileDma<WAVES, kVSwz4, KT> dma(lane, w);
+    const SubVtAddr vad(lane);
     const int head_bytes = a.N * D * 2;
+    constexpr int IPW = SubTileDma<WAVES, kVSwz4, KT>::IPW;
     auto issue = [&](int i, uint8_t* kd, uint8_t* vd) {
+        // every table read comes before the first copy: the compiler cannot tell
+        // the tables from the stage buffers, and an LDS read after a copy would
+        // wait for that copy to land
+        int row[IPW];
 #pragma unroll
-        for (int u = 0; u < SubTileDma<WAVES, kVSwz4, KT>::IPW; ++u) {
-            const int ins = w + WAVES * u;
-            const int p = i * KT + 4 * ins + (lane >> 4);     // 16-key group 4 i + u
-            int row = a.N;                                      // past the head: reads zeros
+        for (int u = 0; u < IPW; ++u) {
+            const int p = i * KT + 4 * (w + WAVES * u) + (lane >> 4);   // 16-key group 4 i + u
+            row[u] = a.N;                                              // past the head: reads zeros
             if (p < L) {
                 const int d = gd[p >> 4];
                 if (d != INT_MIN) {
-                    row = d + p;
-                } else {                                        // the group spans entries: walk
+                    row[u] = d + p;
+                } else {                                               // the group spans entries: walk
                     int e = t0[i];
                     while (e + 1 < cnt && pp[e + 1] <= p) ++e;
-                    row = kst[e] + (p - pp[e]);
+                    row[u] = kst[e] + (p - pp[e]);
                 }
             }
-            dma16(a.k + head_off, head_bytes, kd + ins * 1024, row * 256 + dma.ck[u % SubTileDma<WAVES, kVSwz4, KT>::NCLS], 0);
-            dma16(a.v + head_off, head_bytes, vd + ins * 1024, row * 256 + dma.cv, 0);
+        }
+#pragma unroll
+        for (int u = 0; u < IPW; ++u) {
+            const int ins = w + WAVES * u;
+            dma16(a.k + head_off, head_bytes, kd + ins * 1024, row[u] * 256 + dma.ck[u % SubTileDma<WAVES, kVSwz4, KT>::NCLS], 0);
+            dma16(a.v + head_off, head_bytes, vd + ins * 1024, row[u] * 256 + dma.cv, 0);
         }
     };
 
@@ -328,7 +337,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
             for (int st = 0; st < NST; ++st)
 #pragma unroll
                 for (int g = 0; g < 2; ++g)
-                    o_acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sub_vt_operand(vt, dt, st, g, lane),
+                    o_acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sub_vt_operand(vt, dt, st, g, vad),
                                                                         pf[st][g], o_acc[dt], 0, 0, 0);
     };
 

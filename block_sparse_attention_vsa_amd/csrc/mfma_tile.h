@@ -178,6 +178,14 @@ __device__ __forceinline__ void dma16(const void* base, int nbytes, void* lds_ds
                                              0);
 }
 
+// Workgroup barrier for LDS data only: this wave's LDS reads and writes finish,
+// then the waves meet. Unlike __syncthreads it does not wait for vector-memory
+// loads, so LDS copies of a later stage stay in flight across it. Only for
+// exchanging data written with ordinary LDS stores, never for a DMA'd stage.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // Load of a wave-uniform int32 through the constant address space: a scalar
 // load, waited on with lgkmcnt, so it never waits for vector-memory traffic
 // such as the LDS DMA.
@@ -305,16 +313,32 @@ __device__ __forceinline__ void sub_scores(f32x16 (&s)[NST], const uint8_t* kt, 
 // point at 16 consecutive channels (32 dt + 16 (G & 1) + [0, 16)) of key
 // 32 st + 16 g + 8 r + 4 (G >> 1) + j; lane i then holds channel i of those four
 // keys, which are the keys of k slots (G >> 1, 4 r + j) of the P^T operand.
-__device__ __forceinline__ bf16x8 sub_vt_operand(const uint8_t* vt, int dt, int st, int g, int lane) {
-    constexpr int D = 128;
-    const int G = lane >> 4, gi = lane & 15;
-    const int j = gi >> 2, c = gi & 3;
-    const int chunk = 4 * dt + 2 * (G & 1) + (c >> 1);
+//
+// The key's swizzle term (key & 3) is j for every st, g, r, so a lane's byte
+// offset is one value per dt plus the constant 256 (32 st + 16 g + 8 r).
+// SubVtAddr holds those four values, hidden from the optimiser: with the
+// swizzle visible it re-associates the address so that the reads lose track of
+// which stage array they touch, and every transposed read after the first then
+// waits for all LDS copies in flight, the next stage's prefetch included.
+struct SubVtAddr {
+    int tr[4];
+    __device__ __forceinline__ explicit SubVtAddr(int lane) {
+        const int G = lane >> 4, gi = lane & 15;
+        const int j = gi >> 2, c = gi & 3;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+            const int chunk = 4 * dt + 2 * (G & 1) + (c >> 1);
+            tr[dt] = (4 * (G >> 1) + j) * 256 + ((chunk ^ (4 * j)) << 4) + (c & 1) * 8;
+            asm("" : "+v"(tr[dt]));
+        }
+    }
+};
+
+__device__ __forceinline__ bf16x8 sub_vt_operand(const uint8_t* vt, int dt, int st, int g, const SubVtAddr& ad) {
     v4i16 part[2];
 #pragma unroll
     for (int r2 = 0; r2 < 2; ++r2) {
-        const int key = 32 * st + 16 * g + 8 * r2 + 4 * (G >> 1) + j;
-        const uint8_t* ptr = vt + key * D * 2 + ((chunk ^ (4 * (key & 3))) << 4) + (c & 1) * 8;
+        const uint8_t* ptr = vt + (32 * st + 16 * g + 8 * r2) * 256 + ad.tr[dt];
         part[r2] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(ptr));
     }
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7));
