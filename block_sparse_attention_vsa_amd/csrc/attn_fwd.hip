@@ -236,7 +236,8 @@ __global__ __launch_bounds__(BS * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
     extern __shared__ __attribute__((aligned(16))) int16_t list_lds[];
     __shared__ int wave_cnt[WAVES];
 
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: LDS copy targets stay scalar
     const int l32 = lane & 31, half = lane >> 5;
     const int nqb = a.nb, nkb = a.nb;
     const int item = xcd_remap(blockIdx.x, a.num_items);

@@ -181,7 +181,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
     int32_t* gd = t0 + a.max_subs;
     int16_t* list16 = reinterpret_cast<int16_t*>(gd + 4 * a.max_subs);
 
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: LDS copy targets stay scalar
     const int l32 = lane & 31, half = lane >> 5;
     if ((int)blockIdx.x >= ld_const(a.n_items, 0)) return;     // past the last chunk (uniform)
     const int item = ld_const(a.order, (int)blockIdx.x);
@@ -250,6 +251,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
     const SubVtAddr vad(lane);
     const int head_bytes = a.N * D * 2;
     constexpr int IPW = SubTileDma<WAVES, kVSwz4, KT>::IPW;
+    static_assert(WAVES == 4 && IPW == 4, "copy instruction u of a wave covers 16-key group u of the sub-tile");
+    // copy instruction u of wave w covers keys 4 w + (lane >> 4) of the sub-tile's
+    // 16-key group u, so the group, and its entry in gd, are wave-uniform
+    const int key_in_group = 4 * w + (lane >> 4);
     auto issue = [&](int i, uint8_t* kd, uint8_t* vd) {
         // every table read comes before the first copy: the compiler cannot tell
         // the tables from the stage buffers, and an LDS read after a copy would
@@ -257,13 +262,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
         int row[IPW];
 #pragma unroll
         for (int u = 0; u < IPW; ++u) {
-            const int p = i * KT + 4 * (w + WAVES * u) + (lane >> 4);   // 16-key group 4 i + u
-            row[u] = a.N;                                              // past the head: reads zeros
-            if (p < L) {
-                const int d = gd[p >> 4];
-                if (d != INT_MIN) {
-                    row[u] = d + p;
-                } else {                                               // the group spans entries: walk
+            const int g16 = 4 * i + u;
+            const int p = 16 * g16 + key_in_group;
+            const int d = __builtin_amdgcn_readfirstlane(gd[g16]);
+            if (d != INT_MIN) {
+                row[u] = p < L ? d + p : a.N;                         // past the packed keys: zeros
+            } else {                                                  // the group spans entries: walk
+                row[u] = a.N;
+                if (p < L) {
                     int e = t0[i];
                     while (e + 1 < cnt && pp[e + 1] <= p) ++e;
                     row[u] = kst[e] + (p - pp[e]);
