@@ -278,6 +278,7 @@ __global__ __launch_bounds__(BS * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
     };
     const SubTileDma<WAVES, kVSwz4, KT> dma(lane, w);
     const SubVtAddr vad(lane);
+    const SubKAddr kad(lane);
     const int head_bytes = a.N * D * 2;
     // natural rows / rows through the frame-major map; the main loop below is
     // instantiated once per form, so a natural head runs no gather code
@@ -312,7 +313,7 @@ __global__ __launch_bounds__(BS * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
         if (!wave_active || vs == 0) return;
         // ---- S^T = K Q^T (NST x 32 keys) --------------------------------------
         f32x16 s[NST];
-        sub_scores<NST>(s, kt, qf, l32, half);
+        sub_scores_ahead<NST>(s, kt, qf, kad);
         if (vs < KT) {
 #pragma unroll
             for (int st = 0; st < NST; ++st)
@@ -354,14 +355,7 @@ __global__ __launch_bounds__(BS * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
             }
         l_run += (ps[0] + ps[1]) + (ps[2] + ps[3]);
         // ---- O^T += V^T P^T, V^T through transposing LDS reads -------------------
-#pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-            for (int st = 0; st < NST; ++st)
-#pragma unroll
-                for (int g = 0; g < 2; ++g)
-                    o_acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sub_vt_operand(vt, dt, st, g, vad),
-                                                                        pf[st][g], o_acc[dt], 0, 0, 0);
+        sub_pv_ahead<NST>(o_acc, vt, pf, vad);
     };
 
     const int n_sub = cnt * SUB;

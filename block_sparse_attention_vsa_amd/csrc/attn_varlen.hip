@@ -249,6 +249,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
 
     const SubTileDma<WAVES, kVSwz4, KT> dma(lane, w);
     const SubVtAddr vad(lane);
+    const SubKAddr kad(lane);
     const int head_bytes = a.N * D * 2;
     constexpr int IPW = SubTileDma<WAVES, kVSwz4, KT>::IPW;
     static_assert(WAVES == 4 && IPW == 4, "copy instruction u of a wave covers 16-key group u of the sub-tile");
@@ -299,7 +300,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
         const int vs = min(KT, L - i * KT);
         if (!wave_active) return;
         f32x16 s[NST];
-        sub_scores<NST>(s, kt, qf, l32, half);
+        sub_scores_ahead<NST>(s, kt, qf, kad);
         if (vs < KT) {
 #pragma unroll
             for (int st = 0; st < NST; ++st)
@@ -337,14 +338,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
                 pf[st][x >> 3][x & 7] = (__bf16)p;
             }
         l_run += (ps[0] + ps[1]) + (ps[2] + ps[3]);
-#pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-            for (int st = 0; st < NST; ++st)
-#pragma unroll
-                for (int g = 0; g < 2; ++g)
-                    o_acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sub_vt_operand(vt, dt, st, g, vad),
-                                                                        pf[st][g], o_acc[dt], 0, 0, 0);
+        sub_pv_ahead<NST>(o_acc, vt, pf, vad);
     };
 
     if (n_sub > 0) issue(0, k0, v0);

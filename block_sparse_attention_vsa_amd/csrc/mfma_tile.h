@@ -344,6 +344,87 @@ __device__ __forceinline__ bf16x8 sub_vt_operand(const uint8_t* vt, int dt, int 
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
+// Row-operand offsets of a K sub-tile (row 32 st + l32, chunk 2 kk + half at slot
+// chunk ^ (row & 15); the st term adds 8192), opaque for the same reason as SubVtAddr.
+struct SubKAddr {
+    int rows[8];
+    __device__ __forceinline__ explicit SubKAddr(int lane) {
+        const int l32 = lane & 31, half = lane >> 5;
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) {
+            rows[kk] = l32 * 256 + (((2 * kk + half) ^ (l32 & 15)) << 4);
+            asm("" : "+v"(rows[kk]));
+        }
+    }
+};
+
+// sub_scores with the NST chains side by side and each step's K operands read
+// one step ahead: the scheduler is told to issue the reads of step kk + 1 before
+// the MFMAs of step kk, so an MFMA does not wait on the LDS latency of its own read.
+template <int NST>
+__device__ __forceinline__ void sub_scores_ahead(f32x16 (&s)[NST], const uint8_t* kt, const bf16x8 (&qf)[8],
+                                                 const SubKAddr& ad) {
+#pragma unroll
+    for (int st = 0; st < NST; ++st) s[st] = f32x16{};
+    u32x4 kb[2][NST];
+#pragma unroll
+    for (int st = 0; st < NST; ++st) kb[0][st] = *reinterpret_cast<const u32x4*>(kt + 8192 * st + ad.rows[0]);
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+        if (kk + 1 < 8) {
+#pragma unroll
+            for (int st = 0; st < NST; ++st)
+                kb[(kk + 1) & 1][st] = *reinterpret_cast<const u32x4*>(kt + 8192 * st + ad.rows[kk + 1]);
+        }
+#pragma unroll
+        for (int st = 0; st < NST; ++st)
+            s[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kb[kk & 1][st]), qf[kk], s[st],
+                                                            0, 0, 0);
+    }
+    // groups: 0x100 = LDS reads, 0x008 = MFMA; sync id 1 keeps this sequence apart
+    __builtin_amdgcn_sched_group_barrier(0x100, NST, 1);
+#pragma unroll
+    for (int kk = 0; kk < 7; ++kk) {
+        __builtin_amdgcn_sched_group_barrier(0x100, NST, 1);
+        __builtin_amdgcn_sched_group_barrier(0x008, NST, 1);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, NST, 1);
+}
+
+// O^T += V^T P^T over the 4 channel tiles, the V^T operands of tile dt + 1 read
+// while the MFMAs of tile dt run (same scheduling hint as above, sync id 2).
+template <int NST>
+__device__ __forceinline__ void sub_pv_ahead(f32x16 (&o_acc)[4], const uint8_t* vt, const bf16x8 (&pf)[NST][2],
+                                             const SubVtAddr& ad) {
+    bf16x8 vb[2][NST][2];
+#pragma unroll
+    for (int st = 0; st < NST; ++st)
+#pragma unroll
+        for (int g = 0; g < 2; ++g) vb[0][st][g] = sub_vt_operand(vt, 0, st, g, ad);
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+        if (dt + 1 < 4) {
+#pragma unroll
+            for (int st = 0; st < NST; ++st)
+#pragma unroll
+                for (int g = 0; g < 2; ++g) vb[(dt + 1) & 1][st][g] = sub_vt_operand(vt, dt + 1, st, g, ad);
+        }
+#pragma unroll
+        for (int st = 0; st < NST; ++st)
+#pragma unroll
+            for (int g = 0; g < 2; ++g)
+                o_acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vb[dt & 1][st][g], pf[st][g], o_acc[dt], 0, 0, 0);
+    }
+    // two transposing reads per operand, 2 NST operands per channel tile
+    __builtin_amdgcn_sched_group_barrier(0x100, 4 * NST, 2);
+#pragma unroll
+    for (int dt = 0; dt < 3; ++dt) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 4 * NST, 2);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2 * NST, 2);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2 * NST, 2);
+}
+
 }  // namespace vsa
 
 namespace vsa {
