@@ -27,6 +27,89 @@
 
 namespace vsa {
 
+// The TileAddr products of mfma_tile.h with each operand read issued one step ahead of
+// the MFMA that consumes it (scheduling groups: 0x100 LDS reads, 0x008 MFMA),
+// so the MFMAs do not each wait out the LDS latency of their own read.
+
+// Two row-operand chains over the same 32-row half-tile st of two tiles:
+// a = tile_a rows x frag_a, b = tile_b rows x frag_b, interleaved.
+template <int SWZA, int SWZB>
+__device__ __forceinline__ void tile_rows_mma2_ahead(f32x16& a, f32x16& b, const uint8_t* tile_a, const uint8_t* tile_b,
+                                                     int st, const bf16x8 (&frag_a)[8], const bf16x8 (&frag_b)[8],
+                                                     const TileAddr<SWZA>& ad_a, const TileAddr<SWZB>& ad_b) {
+    a = f32x16{};
+    b = f32x16{};
+    u32x4 ra[2], rb[2];
+    ra[0] = *reinterpret_cast<const u32x4*>(tile_a + 8192 * st + ad_a.rows[0]);
+    rb[0] = *reinterpret_cast<const u32x4*>(tile_b + 8192 * st + ad_b.rows[0]);
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+        if (kk + 1 < 8) {
+            ra[(kk + 1) & 1] = *reinterpret_cast<const u32x4*>(tile_a + 8192 * st + ad_a.rows[kk + 1]);
+            rb[(kk + 1) & 1] = *reinterpret_cast<const u32x4*>(tile_b + 8192 * st + ad_b.rows[kk + 1]);
+        }
+        a = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ra[kk & 1]), frag_a[kk], a, 0, 0, 0);
+        b = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, rb[kk & 1]), frag_b[kk], b, 0, 0, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+#pragma unroll
+    for (int kk = 0; kk < 7; ++kk) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 1);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 1);
+}
+
+// One row-operand chain (tile_rows_mma_at with reads one step ahead).
+template <int SWZ>
+__device__ __forceinline__ f32x16 tile_rows_mma_ahead(const uint8_t* tile, int st, const bf16x8 (&frag)[8],
+                                                      const TileAddr<SWZ>& ad) {
+    f32x16 s = f32x16{};
+    u32x4 r[2];
+    r[0] = *reinterpret_cast<const u32x4*>(tile + 8192 * st + ad.rows[0]);
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+        if (kk + 1 < 8) r[(kk + 1) & 1] = *reinterpret_cast<const u32x4*>(tile + 8192 * st + ad.rows[kk + 1]);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, r[kk & 1]), frag[kk], s, 0, 0, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
+#pragma unroll
+    for (int kk = 0; kk < 7; ++kk) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+    return s;
+}
+
+// acc[dt] += (transposed tile, keys 32 st + [0, 32)) x frag[g] over dt and g, in
+// the order dt, g; the operands of dt + 1 are read while dt's MFMAs run.
+template <int SWZ>
+__device__ __forceinline__ void tile_tr_mma_ahead(f32x16 (&acc)[4], const uint8_t* tile, int st,
+                                                  const bf16x8 (&frag)[2], const TileAddr<SWZ>& ad) {
+    bf16x8 op[2][2];
+#pragma unroll
+    for (int g = 0; g < 2; ++g) op[0][g] = tile_tr_operand_at(tile, 0, st, g, ad);
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+        if (dt + 1 < 4) {
+#pragma unroll
+            for (int g = 0; g < 2; ++g) op[(dt + 1) & 1][g] = tile_tr_operand_at(tile, dt + 1, st, g, ad);
+        }
+#pragma unroll
+        for (int g = 0; g < 2; ++g)
+            acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[dt & 1][g], frag[g], acc[dt], 0, 0, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 2);
+#pragma unroll
+    for (int dt = 0; dt < 3; ++dt) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 2);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 2);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 2);
+}
+
+
 constexpr int kBwdMaxMask = 4096;      // key blocks per mask row (mask form)
 
 struct BwdArgs {
@@ -240,8 +323,8 @@ __global__ __launch_bounds__(BS * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
         // one 32-key half at a time keeps the live scores within the register budget
 #pragma unroll
         for (int st = 0; st < NST; ++st) {
-            const f32x16 s = tile_rows_mma_at(kt, st, qf, adk);      // S^T = K Q^T
-            const f32x16 dp = tile_rows_mma_at(vt, st, dof, adv);    // dP^T = V dO^T
+            f32x16 s, dp;                                            // S^T = K Q^T, dP^T = V dO^T
+            tile_rows_mma2_ahead(s, dp, kt, vt, st, qf, dof, adk, adv);
             bf16x8 dsf[2];
 #pragma unroll
             for (int x = 0; x < 16; ++x) {
@@ -249,12 +332,8 @@ __global__ __launch_bounds__(BS * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
                 if (acc_key(st, x, half) >= vs) p = 0.f;
                 dsf[x >> 3][x & 7] = (__bf16)(p * (dp[x] - dlt));
             }
-#pragma unroll
-            for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-                for (int g = 0; g < 2; ++g)
-                    acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tile_tr_operand_at(kt, dt, st, g, adk), dsf[g],
-                                                                      acc[dt], 0, 0, 0);
+            tile_tr_mma_ahead(acc, kt, st, dsf, adk);                // dQ^T += K^T dS^T
+            __builtin_amdgcn_sched_barrier(0);                       // keep each half's read order to itself
         }
     };
 
@@ -346,7 +425,7 @@ __global__ __launch_bounds__(BS * 4) __attribute__((amdgpu_waves_per_eu(2))) voi
             if (!ds_wave) {
 #pragma unroll
                 for (int st = 0; st < NST; ++st) {
-                    const f32x16 s = tile_rows_mma_at(qt, st, kv, ad);          // S = Q K^T: lane = key
+                    const f32x16 s = tile_rows_mma_ahead(qt, st, kv, ad);       // S = Q K^T: lane = key
 #pragma unroll
                     for (int xg = 0; xg < 4; ++xg) {
                         // queries 32 st + 8 xg + 4 half + [0, 4) of the sub-tile
@@ -363,7 +442,7 @@ __global__ __launch_bounds__(BS * 4) __attribute__((amdgpu_waves_per_eu(2))) voi
                 }
             } else {
 #pragma unroll
-                for (int st = 0; st < NST; ++st) dp[st] = tile_rows_mma_at(ot, st, kv, ad);   // dP = dO V^T
+                for (int st = 0; st < NST; ++st) dp[st] = tile_rows_mma_ahead(ot, st, kv, ad);   // dP = dO V^T
             }
         }
         lds_barrier();                                // P visible to the dS waves; the next stage's copy runs on
@@ -371,13 +450,10 @@ __global__ __launch_bounds__(BS * 4) __attribute__((amdgpu_waves_per_eu(2))) voi
         if (!active) return;
         if (!ds_wave) {
 #pragma unroll
-            for (int st = 0; st < NST; ++st)
-#pragma unroll
-                for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-                    for (int g = 0; g < 2; ++g)
-                        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tile_tr_operand_at(ot, dt, st, g, ad),
-                                                                          pf[st][g], acc[dt], 0, 0, 0);
+            for (int st = 0; st < NST; ++st) {
+                tile_tr_mma_ahead(acc, ot, st, pf[st], ad);                    // dV^T += dO^T P
+                __builtin_amdgcn_sched_barrier(0);
+            }
         } else {
 #pragma unroll
             for (int st = 0; st < NST; ++st) {
@@ -390,12 +466,8 @@ __global__ __launch_bounds__(BS * 4) __attribute__((amdgpu_waves_per_eu(2))) voi
                     for (int e = 0; e < 4; ++e)
                         dsf[xg >> 1][4 * (xg & 1) + e] = (__bf16)(p4[e] * (dp[st][4 * xg + e] - d4[e]));
                 }
-#pragma unroll
-                for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-                    for (int g = 0; g < 2; ++g)
-                        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tile_tr_operand_at(qt, dt, st, g, ad),
-                                                                          dsf[g], acc[dt], 0, 0, 0);
+                tile_tr_mma_ahead(acc, qt, st, dsf, ad);                        // dK^T += Q^T dS
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
     };
