@@ -314,6 +314,8 @@ __global__ __launch_bounds__(BS * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
         // ---- S^T = K Q^T (NST x 32 keys) --------------------------------------
         f32x16 s[NST];
         sub_scores_ahead<NST>(s, kt, qf, kad);
+        bf16x8 vfirst[NST][2];
+        sub_pv_first<NST>(vfirst, vt, vad);
         if (vs < KT) {
 #pragma unroll
             for (int st = 0; st < NST; ++st)
@@ -355,7 +357,7 @@ __global__ __launch_bounds__(BS * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
             }
         l_run += (ps[0] + ps[1]) + (ps[2] + ps[3]);
         // ---- O^T += V^T P^T, V^T through transposing LDS reads -------------------
-        sub_pv_ahead<NST>(o_acc, vt, pf, vad);
+        sub_pv_ahead<NST>(o_acc, vt, pf, vfirst, vad);
     };
 
     const int n_sub = cnt * SUB;

@@ -301,6 +301,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
         if (!wave_active) return;
         f32x16 s[NST];
         sub_scores_ahead<NST>(s, kt, qf, kad);
+        bf16x8 vfirst[NST][2];
+        sub_pv_first<NST>(vfirst, vt, vad);
         if (vs < KT) {
 #pragma unroll
             for (int st = 0; st < NST; ++st)
@@ -338,7 +340,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
                 pf[st][x >> 3][x & 7] = (__bf16)p;
             }
         l_run += (ps[0] + ps[1]) + (ps[2] + ps[3]);
-        sub_pv_ahead<NST>(o_acc, vt, pf, vad);
+        sub_pv_ahead<NST>(o_acc, vt, pf, vfirst, vad);
     };
 
     if (n_sub > 0) issue(0, k0, v0);

@@ -391,16 +391,27 @@ __device__ __forceinline__ void sub_scores_ahead(f32x16 (&s)[NST], const uint8_t
     __builtin_amdgcn_sched_group_barrier(0x008, NST, 1);
 }
 
-// O^T += V^T P^T over the 4 channel tiles, the V^T operands of tile dt + 1 read
-// while the MFMAs of tile dt run (same scheduling hint as above, sync id 2).
+// V^T operands of channel tile 0: they do not depend on P, so the caller reads
+// them before the softmax and the reads overlap it.
+template <int NST>
+__device__ __forceinline__ void sub_pv_first(bf16x8 (&first)[NST][2], const uint8_t* vt, const SubVtAddr& ad) {
+#pragma unroll
+    for (int st = 0; st < NST; ++st)
+#pragma unroll
+        for (int g = 0; g < 2; ++g) first[st][g] = sub_vt_operand(vt, 0, st, g, ad);
+}
+
+// O^T += V^T P^T over the 4 channel tiles (tile 0's operands from sub_pv_first),
+// the V^T operands of tile dt + 1 read while the MFMAs of tile dt run (same
+// scheduling hint as above, sync id 2).
 template <int NST>
 __device__ __forceinline__ void sub_pv_ahead(f32x16 (&o_acc)[4], const uint8_t* vt, const bf16x8 (&pf)[NST][2],
-                                             const SubVtAddr& ad) {
+                                             const bf16x8 (&first)[NST][2], const SubVtAddr& ad) {
     bf16x8 vb[2][NST][2];
 #pragma unroll
     for (int st = 0; st < NST; ++st)
 #pragma unroll
-        for (int g = 0; g < 2; ++g) vb[0][st][g] = sub_vt_operand(vt, 0, st, g, ad);
+        for (int g = 0; g < 2; ++g) vb[0][st][g] = first[st][g];
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) {
         if (dt + 1 < 4) {
@@ -416,7 +427,6 @@ __device__ __forceinline__ void sub_pv_ahead(f32x16 (&o_acc)[4], const uint8_t* 
                 o_acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vb[dt & 1][st][g], pf[st][g], o_acc[dt], 0, 0, 0);
     }
     // two transposing reads per operand, 2 NST operands per channel tile
-    __builtin_amdgcn_sched_group_barrier(0x100, 4 * NST, 2);
 #pragma unroll
     for (int dt = 0; dt < 3; ++dt) {
         __builtin_amdgcn_sched_group_barrier(0x100, 4 * NST, 2);
