@@ -320,7 +320,7 @@ def main():
     perm_gbs = 2 * q.numel() * q.element_size() / (perm_ms * 1e-3) / 1e9
     del pdst
 
-    # the step's attention launch alone, warm and cold, and what the box reaches on plain work
+    # the step's attention launch alone, warm and cold, and what this GPU reaches on plain work
     kstats = launch_stats(torch, T, lambda: V.vsa_block_sparse_attn_fwd_chosen(q, k, v, grid, bs, cand, [0, 1], ch),
                           flops)
     achievable = achievable_peaks(torch, T)
@@ -412,7 +412,7 @@ def launch_stats(torch, T, fn, flops, runs=50, warm=5, flush_bytes=1 << 30):
 
 
 def achievable_peaks(torch, T):
-    """What this machine reaches on plain work: a bf16 GEMM (torch / hipBLASLt,
+    """What this GPU reaches on plain work: a bf16 GEMM (torch / hipBLASLt,
     8192^3) and a 1 GiB device-to-device copy."""
     dev = torch.device("cuda:0")
     n = 8192
