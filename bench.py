@@ -31,7 +31,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 from workloads import (WAN480, WAN480_CUBE, WAN480_SEMANTIC, LONG126, HUNYUAN720, make_qkv,  # noqa: E402
-                       profile_rows)
+                       profile_rows, rng)
 
 PEAK_BF16_TFLOPS = 2516.6       # MI355X dense bf16 MFMA
 PEAK_FP8_TFLOPS = 5033.2        # MI355X dense fp8 MFMA
@@ -78,7 +78,8 @@ def _cpu_unit(args):
 
 def cpu_leg(args):
     """Child program (never touches the GPU): regenerates the step's inputs, builds
-    the two candidate masks with the oracle and times the oracle's attention."""
+    the two candidate masks with the oracle and times the oracle's attention, then
+    the oracle's other steps on small samples (one JSON line each)."""
     from oracle.masks import pattern_mask
     w = WAN480
     q, k, v = make_qkv(w)
@@ -86,17 +87,64 @@ def cpu_leg(args):
     m_s = pattern_mask(w.grid, w.bs, "spatial", w.extra["w_spatial"])
     m_t = pattern_mask(w.grid, w.bs, "temporal", w.extra["w_temporal"])
     print(json.dumps(cpu_baseline(q, k, v, choice, m_s, m_t, args.cpu_sample_blocks)), flush=True)
+    print(json.dumps(cpu_rows(q, k, v, m_s, m_t)), flush=True)
+
+
+def cpu_rows(q, k, v, m_s, m_t):
+    """The oracle's other steps of the layer, each on a bounded sample, in this one
+    process: wall time of the call as it stands (fp64 numpy)."""
+    from oracle.layout import permute
+    from oracle.masks import pattern_mask
+    from oracle.profile import profile_heads
+    from oracle.scores import block_scores
+    from oracle.select import select
+    w = WAN480
+    N, D = w.N, w.D
+
+    def wall(fn):
+        t0 = time.perf_counter()
+        fn()
+        return time.perf_counter() - t0
+
+    out = {}
+    t = wall(lambda: (pattern_mask(w.grid, w.bs, "spatial", w.extra["w_spatial"]),
+                      pattern_mask(w.grid, w.bs, "temporal", w.extra["w_temporal"])))
+    out["a1_pattern_masks"] = {"ms": round(t * 1e3, 3), "sample": "both candidate masks of the Wan grid (all of a1)"}
+    t = wall(lambda: permute(q[:, :1], w.grid, "frame_major"))
+    out["a3_permute"] = {"ms": round(t * 1e3, 3), "GBps": round(2 * N * D * 2 / t / 1e9, 3),
+                         "sample": "frame-major move of one head of Q (32,760 x 128), bytes counted as bf16 read + write"}
+    t = wall(lambda: block_scores(q[:, :1], k[:, :1], w.bs))
+    out["a4_block_scores"] = {"ms": round(t * 1e3, 3), "sample": "pooling and pooled scores of one head, bs 128"}
+    nc = WAN480_CUBE.extra.get("cube", 4)
+    ncube = -(-w.T // nc) * -(-w.Hh // nc) * -(-w.W // nc)
+    sc = rng(0, 99).standard_normal((1, 1, ncube, ncube))
+    k_max = int(WAN480_CUBE.extra["k_frac"] * ncube)
+    t = wall(lambda: select(sc, None, k_max, WAN480_CUBE.extra["top_p"]))
+    out["a5_select"] = {"ms": round(t * 1e3, 3),
+                        "sample": f"top-p {WAN480_CUBE.extra['top_p']} / k_max {k_max} over one head's {ncube} x {ncube} "
+                                  "cube scores (seeded normal scores)"}
+    rows = profile_rows(w, w.extra["profile_frac"])
+    sub = rows[:: max(1, rows.size // 32)][:32]
+    t = wall(lambda: profile_heads(q[:, :1], k[:, :1], v[:, :1], w.grid, w.bs, sub, [m_s, m_t], [0, 1]))
+    out["a2_profile"] = {"ms": round(t * 1e3, 3), "ms_per_row": round(t * 1e3 / sub.size, 3),
+                         "sample": f"one head, {sub.size} of the step's {rows.size} sampled rows (the step profiles "
+                                   f"{w.H} x {rows.size} rows), dense output and both candidates"}
+    out["what"] = ("the oracle's other steps timed beside this run's GPU figures (components_ms, permute_standalone, "
+                   "extra_layers.cube_topp_wan480); one process, fp64")
+    return out
 
 
 def run_cpu_leg(choice, blocks_per_head):
+    """(cpu_baseline, oracle row timings) from the child program, or (None, None)."""
     import subprocess
     cmd = [sys.executable, os.path.abspath(__file__), "--cpu-leg", "--choice", ",".join(str(int(c)) for c in choice),
            "--cpu-sample-blocks", str(blocks_per_head)]
     res = subprocess.run(cmd, capture_output=True, text=True, timeout=600)
     if res.returncode != 0:
         print(f"bench.py: CPU baseline leg failed:\n{res.stderr[-2000:]}", file=sys.stderr)
-        return None
-    return json.loads(res.stdout.strip().splitlines()[-1])
+        return None, None
+    lines = [ln for ln in res.stdout.strip().splitlines() if ln.startswith("{")]
+    return json.loads(lines[0]), (json.loads(lines[1]) if len(lines) > 1 else None)
 
 
 def cpu_baseline(q, k, v, choice, m_s, m_t, blocks_per_head):
@@ -340,9 +388,9 @@ def main():
                 "avg_launch_ms": round(attn_ms, 4),
                 "frac_of_achievable": round(attn_tflops / achievable["bf16_gemm_tflops"], 4)}
 
-    cpu = None
+    cpu, cpu_steps = None, None
     if not args.no_cpu_baseline:
-        cpu = run_cpu_leg(sel, args.cpu_sample_blocks)
+        cpu, cpu_steps = run_cpu_leg(sel, args.cpu_sample_blocks)
 
     if args.copy_calibration_mib:
         src = torch.empty((args.copy_calibration_mib << 20,), dtype=torch.uint8, device=dev)
@@ -377,6 +425,7 @@ def main():
         "extra_layers": extra,
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "cpu_oracle_steps": cpu_steps,
     }
     print(json.dumps(out), flush=True)
 
