@@ -101,11 +101,30 @@ __global__ __launch_bounds__(256) void prof_bits_kernel(BitsArgs a) {
         const int lay = a.layout[p];
         const uint32_t qblk = a.div_bs.div(layout_pos(a, lay, (uint32_t)r));
         const uint8_t* mrow = a.masks + ((int64_t)p * a.nb + qblk) * a.nb;
+        if (lay == 0 && (a.bs & 31) == 0) {
+            // natural order, blocks a multiple of 32 keys: the word's keys share one block
+            const int valid = min(32, a.N - 32 * wi);
+            if (mrow[(32 * wi) / a.bs]) word = valid == 32 ? 0xffffffffu : (1u << valid) - 1u;
+        } else if (lay == 0) {
 #pragma unroll
-        for (int b = 0; b < 32; ++b) {
-            const uint32_t n = (uint32_t)min(32 * wi + b, a.N - 1);      // clamped: loaded, then dropped
-            const uint8_t m = mrow[a.div_bs.div(layout_pos(a, lay, n))];
-            if (m && 32 * wi + b < a.N) word |= 1u << b;
+            for (int b = 0; b < 32; ++b)
+                if (32 * wi + b < a.N && mrow[a.div_bs.div((uint32_t)(32 * wi + b))]) word |= 1u << b;
+        } else {
+            // frame-major: (t, s) of the word's first key, then stepped key by key
+            // (one division per word instead of one per key)
+            const uint32_t n0 = 32u * (uint32_t)wi;
+            uint32_t t = a.div_HW.div(n0), sp = n0 - t * (uint32_t)a.HW;
+#pragma unroll
+            for (int b = 0; b < 32; ++b) {
+                const bool in = 32 * wi + b < a.N;
+                const uint32_t pos = in ? sp * (uint32_t)a.T + t : 0u;       // dropped past N
+                const uint8_t m = mrow[a.div_bs.div(pos)];
+                if (m && in) word |= 1u << b;
+                if (++sp == (uint32_t)a.HW) {
+                    sp = 0;
+                    ++t;
+                }
+            }
         }
     }
     a.bits[e] = word;
