@@ -665,7 +665,9 @@ def extra_layers(torch, V, PL, T):
     q, k, v = (torch.from_numpy(x).to(torch.bfloat16).to(dev) for x in make_qkv(w))
     n_cubes, k_max = PL.cube_budget(w.grid, w.extra["k_frac"])
     blk = V.vsa_cube_block_len(w.grid)
-    times = {}
+    times, reps = {}, []
+    # no host sync inside the loop: the host queues ahead, so each event pair
+    # brackets GPU work only, not the host's launch latency
     for rep in range(4):
         e = [T.ev()]
         qc = V.vsa_permute(q, w.grid, V.VSA_PERM_CUBE4)
@@ -680,14 +682,25 @@ def extra_layers(torch, V, PL, T):
         e.append(T.ev())
         o = V.vsa_permute(oc, w.grid, V.VSA_PERM_CUBE4, inverse=True)
         e.append(T.ev())
-        torch.cuda.synchronize()
         if rep:
-            for key, i in (("a3_cube_permute_qkv", 0), ("a4_block_scores", 1), ("a5_select_topk", 2),
-                           ("a7_attention", 3), ("a8_cube_permute_o", 4)):
-                times.setdefault(key, []).append(e[i].elapsed_time(e[i + 1]))
+            reps.append(e)
+    torch.cuda.synchronize()
+    for e in reps:
+        for key, i in (("a3_cube_permute_qkv", 0), ("a4_block_scores", 1), ("a5_select_topk", 2),
+                       ("a7_attention", 3), ("a8_cube_permute_o", 4)):
+            times.setdefault(key, []).append(e[i].elapsed_time(e[i + 1]))
     fl = kept_flops_from_lists(idx, cnt, oc.shape[2], 64, 128, blk)
     t_att = float(np.mean(times["a7_attention"]))
+    nat_b = q.numel() * q.element_size()                         # one natural-order tensor
+    cube_b = qc.numel() * qc.element_size()                      # one cube-major tensor, pad slots included
+    gbs = {"a3_cube_permute_qkv": 3 * (nat_b + cube_b),          # read every token, write every slot
+           "a4_block_scores": 2 * cube_b + S.numel() * 4,        # Q and K read once, S written
+           "a8_cube_permute_o": cube_b + nat_b}
+    hbm = {key: {"GBps": round(b / (np.mean(times[key]) * 1e-3) / 1e9, 1),
+                 "frac_of_hbm_peak": round(b / (np.mean(times[key]) * 1e-3) / 1e9 / PEAK_HBM_GBS, 3)}
+           for key, b in gbs.items()}
     res["cube_topp_wan480"] = {"ms": {k_: round(float(np.mean(v_)), 4) for k_, v_ in times.items()},
+                               "hbm": hbm,
                                "k_max": k_max, "mean_kept": round(float(cnt.float().mean().item()), 2),
                                "attn_tflops": round(fl / (t_att * 1e-3) / 1e12, 2),
                                "backward": time_backward(torch, V, T, qc, kc, vc, 64, fl, kv_idx=idx, kv_cnt=cnt,
@@ -698,7 +711,7 @@ def extra_layers(torch, V, PL, T):
     w = LONG126
     q, k, v = (torch.from_numpy(x).to(torch.bfloat16).to(dev) for x in make_qkv(w))
     k_total = int(round(w.extra["density"] * w.nb))
-    times = {}
+    times, reps = {}, []
     for rep in range(3):
         e = [T.ev()]
         forced = V.vsa_pattern_mask(w.grid, w.bs, V.VSA_PATTERN_SPATIAL, w.extra["w_local"])
@@ -709,13 +722,19 @@ def extra_layers(torch, V, PL, T):
         e.append(T.ev())
         o = V.vsa_block_sparse_attn_fwd(q, k, v, w.bs, kv_idx=idx, kv_cnt=cnt)
         e.append(T.ev())
-        torch.cuda.synchronize()
         if rep:
-            for key, i in (("a1_local_mask", 0), ("a4_block_scores", 1), ("a5_select_topk", 2), ("a7_attention", 3)):
-                times.setdefault(key, []).append(e[i].elapsed_time(e[i + 1]))
+            reps.append(e)
+    torch.cuda.synchronize()
+    for e in reps:
+        for key, i in (("a1_local_mask", 0), ("a4_block_scores", 1), ("a5_select_topk", 2), ("a7_attention", 3)):
+            times.setdefault(key, []).append(e[i].elapsed_time(e[i + 1]))
     fl = kept_flops_from_lists(idx, cnt, w.N, w.bs, 128)
     t_att = float(np.mean(times["a7_attention"]))
+    a4_b = 2 * q.numel() * q.element_size() + S.numel() * 4      # Q and K read once, S written
+    a4_gbs = a4_b / (np.mean(times["a4_block_scores"]) * 1e-3) / 1e9
     res["long_horizon_126x30x52"] = {"ms": {k_: round(float(np.mean(v_)), 4) for k_, v_ in times.items()},
+                                     "hbm": {"a4_block_scores": {"GBps": round(a4_gbs, 1),
+                                                                 "frac_of_hbm_peak": round(a4_gbs / PEAK_HBM_GBS, 3)}},
                                      "k_total": k_total, "attn_tflops": round(fl / (t_att * 1e-3) / 1e12, 2),
                                      "pct_mfma_peak": round(100 * fl / (t_att * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2)}
     del q, k, v, o, S

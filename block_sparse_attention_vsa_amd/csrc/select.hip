@@ -1,4 +1,4 @@
-// Forced + top-k / top-p key-block selection, one workgroup per (b, h, query
+// Forced + top-k / top-p key-block selection, one wavefront per (b, h, query
 // block) row of pooled scores.
 //
 // USV page, Figure 2 caption: long-range sparse attention over key cubes picked
@@ -7,23 +7,30 @@
 //
 // Each block gets a unique 64-bit rank key [forced:1][order-preserving score
 // bits:32][0x7fffffff - index:31]: larger key = better rank (forced first, then
-// higher score, then lower index). Per row (256 threads, row state in LDS):
-//  1. K = min(k_max, nkb): an MSB-first radix select (8-bit digits, histogram
-//     with integer LDS atomics, wave-level scans) finds the K-th largest key T;
-//     the K best blocks are exactly the keys >= T.
+// higher score, then lower index). A row's keys live in the wave's registers
+// (lane l holds blocks l, l + 64, ...); nothing needs a workgroup barrier:
+//  1. K = min(k_max, nkb): an MSB-first radix select (8-bit digits, 256-bin
+//     LDS histograms, a DPP wave scan over the digits) finds the K-th largest
+//     key T; the K best blocks are exactly the keys >= T.
 //  2. Without top-p (or when forced blocks fill the cap) those K blocks are kept.
-//     With top-p, the K winners are sorted (bitonic, in LDS) and the softmax mass
-//     of the ranked non-forced candidates is accumulated in rank order until it
-//     reaches top_p; softmax is over all nkb scores of the row (fp32, Z summed in
-//     a fixed tree order).
-//  3. Kept blocks are written in ascending index order.
+//     With top-p, softmax is taken over all nkb scores of the row (fp32). The
+//     ranked (non-forced) blocks are kept down to the first one at which the
+//     mass ranked at or above it reaches top_p: a second digit walk whose bins
+//     weigh mass instead of counting keys finds that key X, and the kept set is
+//     the keys >= max(T, X) (the cap wins when X ranks below the K-th key).
+//  3. Kept blocks are written in ascending index order (ballot + popcount).
 #include <math.h>
 
 #include "vsa_internal.h"
 
 namespace vsa {
 
-constexpr int kSelMax = 4096;   // largest row (key blocks) a workgroup holds
+constexpr int kSelMax = 4096;   // largest row (key blocks) one wave holds in registers
+constexpr int kCopies = 4;      // radix histograms per wave
+constexpr int kStride = 257;    // words per histogram copy (odd: copies sit in different banks)
+constexpr int kCopyWords = kCopies * kStride + 3 & ~3;   // 16-byte multiple
+// LDS words per wave: count copies, weight copies, count totals, weight totals
+constexpr int kLdsWords = 2 * kCopyWords + 2 * 256;
 
 __device__ __forceinline__ uint32_t order_bits(float f) {
     uint32_t u = __float_as_uint(f);
@@ -34,159 +41,214 @@ __device__ __forceinline__ float score_of_key(uint64_t key) {
     uint32_t u = (o & 0x80000000u) ? (o & 0x7fffffffu) : ~o;
     return __uint_as_float(u);
 }
-__device__ __forceinline__ int index_of_key(uint64_t key) { return 0x7fffffff - (int)(key & 0x7fffffffull); }
 
-// Fixed-order block reduction over 256 threads.
-__device__ __forceinline__ float block_reduce(float v, float* red, bool is_max) {
-    const int tid = threadIdx.x;
-    red[tid] = v;
-    __syncthreads();
-    for (int s = 128; s > 0; s >>= 1) {
-        if (tid < s) red[tid] = is_max ? fmaxf(red[tid], red[tid + s]) : red[tid] + red[tid + s];
-        __syncthreads();
-    }
-    float r = red[0];
-    __syncthreads();
-    return r;
-}
+// LDS operations of one wave complete in issue order; this keeps the compiler
+// from moving them across the point and waits for those in flight.
+__device__ __forceinline__ void wave_lds_fence() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
-// Inclusive scan of one value per thread over 256 threads (wave scans + totals).
-__device__ __forceinline__ uint32_t block_scan(uint32_t v, uint32_t* wave_tot) {
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+__device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        uint32_t t = __shfl_up(v, off);
-        if (lane >= off) v += t;
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+    return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+    return v;
+}
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+        const uint64_t o = __shfl_xor(v, off);
+        v = o > v ? o : v;
     }
-    if (lane == 63) wave_tot[w] = v;
-    __syncthreads();
-    for (int i = 0; i < w; ++i) v += wave_tot[i];
-    __syncthreads();
     return v;
 }
 
-__global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ scores, int nqb, int nkb, int P2K,
-                                                     const uint8_t* __restrict__ forced, int k_max, float top_p,
-                                                     int32_t* __restrict__ kv_idx, int32_t* __restrict__ kv_cnt) {
-    extern __shared__ __attribute__((aligned(16))) uint8_t dyn[];
-    uint64_t* keys = reinterpret_cast<uint64_t*>(dyn);                 // [nkb]
-    uint64_t* tops = keys + nkb;                                       // [P2K]
-    uint8_t* keep = reinterpret_cast<uint8_t*>(tops + P2K);            // [nkb]
-    __shared__ float red[256];
-    __shared__ uint32_t hist[256];
-    __shared__ uint32_t wave_tot[4];
-    __shared__ uint64_t sel_prefix;
-    __shared__ uint32_t sel_above, sel_bin;
-    __shared__ int n_keep_s, n_top_s;
+// Inclusive scan over the 64 lanes on DPP: shifts by 1, 2, 4, 8 inside each
+// row of 16 lanes, then the last lane of rows 0 and 2 is added to rows 1 and 3,
+// and lane 31 to rows 2 and 3. Integer adds, so the order does not matter.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xf, 0xf, false);
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xf, 0xf, false);
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xf, 0xf, false);
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xf, 0xf, false);
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xa, 0xf, false);
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xc, 0xf, false);
+    return x;
+}
 
-    const int tid = threadIdx.x;
+// One digit of an MSB-first walk over the wave's keys. Among the keys with
+// in[e] set whose bits above `shift + 8` equal `prefix`, bins by the 8-bit digit
+// at `shift` and walks the bins from the top digit down, adding each bin's
+// weight (its key count, or with WEIGHTED the sum of wt[e]). Returns the digit
+// whose bin takes the running total to `need` (-1 if the total stays below),
+// the total of the bins above it and the bin's key count.
+template <int NPL, bool WEIGHTED>
+__device__ __forceinline__ int digit_step(const uint64_t (&key)[NPL], const uint32_t (&wt)[NPL],
+                                          const bool (&in)[NPL], uint64_t prefix, uint64_t pmask, int shift,
+                                          uint32_t need, uint32_t* lds, int lane, uint32_t& above,
+                                          uint32_t& bin_cnt) {
+    uint32_t* cnt_h = lds;
+    uint32_t* wt_h = lds + kCopyWords;
+    uint32_t* cnt_t = lds + 2 * kCopyWords;
+    uint32_t* wt_t = cnt_t + 256;
+    constexpr int clear_words = WEIGHTED ? 2 * kCopyWords : kCopyWords;
+    for (int i = 4 * lane; i < clear_words; i += 256) *reinterpret_cast<u32x4*>(lds + i) = u32x4{0u, 0u, 0u, 0u};
+    wave_lds_fence();
+    const int copy = (lane % kCopies) * kStride;
+#pragma unroll
+    for (int e = 0; e < NPL; ++e)
+        if (in[e] && (key[e] & pmask) == prefix) {
+            const int d = (int)((key[e] >> shift) & 255u);
+            atomicAdd(&cnt_h[copy + d], 1u);
+            if (WEIGHTED) atomicAdd(&wt_h[copy + d], wt[e]);
+        }
+    wave_lds_fence();
+    // fold the copies: lane t sums digits t, t + 64, t + 128, t + 192
+#pragma unroll 1
+    for (int q = 0; q < 4; ++q) {
+        const int d = lane + 64 * q;
+        uint32_t c = 0, w = 0;
+#pragma unroll
+        for (int k = 0; k < kCopies; ++k) {
+            c += cnt_h[k * kStride + d];
+            if (WEIGHTED) w += wt_h[k * kStride + d];
+        }
+        cnt_t[d] = c;
+        if (WEIGHTED) wt_t[d] = w;
+    }
+    wave_lds_fence();
+    // lane t takes digits 255 - 4t ... 252 - 4t: lane order is descending
+    const u32x4 cv = *reinterpret_cast<const u32x4*>(cnt_t + 252 - 4 * lane);
+    const u32x4 wv = WEIGHTED ? *reinterpret_cast<const u32x4*>(wt_t + 252 - 4 * lane) : cv;
+    const uint32_t tot = wv[0] + wv[1] + wv[2] + wv[3];
+    const uint32_t incl = wave_incl_scan(tot);
+    const bool hit = incl - tot < need && incl >= need;      // at most one lane
+    const uint64_t bal = __ballot(hit);
+    wave_lds_fence();
+    if (!bal) return -1;
+    const int src = __ffsll((unsigned long long)bal) - 1;
+    // inside the lane: digits 255 - 4t - q are elements 3 - q of the vectors
+    uint32_t run = incl - tot, ab = 0, bc = 0;
+    int q_hit = 0;
+    bool done = false;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        if (!done && run + wv[3 - q] >= need) { done = true; q_hit = q; ab = run; bc = cv[3 - q]; }
+        else if (!done) run += wv[3 - q];
+    }
+    above = (uint32_t)__shfl((int)ab, src);
+    bin_cnt = (uint32_t)__shfl((int)bc, src);
+    return 255 - 4 * src - __shfl(q_hit, src);
+}
+
+// NPL keys per lane: rows of up to 64 NPL key blocks.
+template <int NPL>
+__global__ __launch_bounds__(64) void select_kernel(const float* __restrict__ scores, int nqb, int nkb,
+                                                    const uint8_t* __restrict__ forced, int k_max, float top_p,
+                                                    int32_t* __restrict__ kv_idx, int32_t* __restrict__ kv_cnt) {
+    __shared__ __attribute__((aligned(16))) uint32_t lds[kLdsWords];
+    const int lane = threadIdx.x;
+    const uint64_t lt = (1ull << lane) - 1ull;
     const int64_t row = blockIdx.x;
     const int qb = (int)(row % nqb);
     const float* s = scores + row * (int64_t)nkb;
     const uint8_t* f = forced ? forced + (int64_t)qb * nkb : nullptr;
-    const bool use_p = top_p < 1.f;
 
+    uint64_t key[NPL];
+    bool in[NPL];
+    uint32_t wt[NPL];
     float mx = -INFINITY;
-    int nf_local = 0;
-    for (int j = tid; j < nkb; j += 256) {
-        const float v = s[j];
-        const bool fj = f && f[j];
-        mx = fmaxf(mx, v);
-        nf_local += fj;
-        keys[j] = ((uint64_t)(fj ? 1u : 0u) << 63) | ((uint64_t)order_bits(v) << 31) |
-                  (uint64_t)(0x7fffffffu - (uint32_t)j);
-        keep[j] = 0;
+    int nf = 0;
+#pragma unroll
+    for (int e = 0; e < NPL; ++e) {
+        const int j = lane + 64 * e;
+        key[e] = 0ull;                                   // below every real key
+        in[e] = j < nkb;
+        wt[e] = 1u;
+        if (j < nkb) {
+            const float v = s[j];
+            const bool fj = f && f[j];
+            mx = fmaxf(mx, v);
+            nf += fj;
+            key[e] = ((uint64_t)(fj ? 1u : 0u) << 63) | ((uint64_t)order_bits(v) << 31) |
+                     (uint64_t)(0x7fffffffu - (uint32_t)j);
+        }
     }
-    const int nforced = (int)block_reduce((float)nf_local, red, false);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) nf += __shfl_xor(nf, off);
+    const int nforced = nf;
     const int K = min(k_max, nkb);
 
     // ---- 1. radix select of the K-th largest key -------------------------------
     uint64_t prefix = 0, pmask = 0;
     uint32_t krem = (uint32_t)K;
+#pragma unroll 1
     for (int shift = 56; shift >= 0; shift -= 8) {
-        hist[tid] = 0;
-        __syncthreads();
-        for (int j = tid; j < nkb; j += 256) {
-            const uint64_t key = keys[j];
-            if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
-        }
-        __syncthreads();
-        // thread t looks at digit 255 - t (descending), cum = count of digits >= it
-        const uint32_t c = hist[255 - tid];
-        const uint32_t cum = block_scan(c, wave_tot);
-        if (cum >= krem && cum - c < krem) {
-            sel_prefix = prefix | ((uint64_t)(255 - tid) << shift);
-            sel_above = cum - c;
-            sel_bin = c;
-        }
-        __syncthreads();
-        prefix = sel_prefix;
+        uint32_t above = 0, bc = 0;
+        const int d = digit_step<NPL, false>(key, wt, in, prefix, pmask, shift, krem, lds, lane, above, bc);
+        prefix |= (uint64_t)d << shift;      // d >= 0: the row holds at least krem matching keys
         pmask |= (uint64_t)0xff << shift;
-        krem -= sel_above;
-        if (sel_bin == krem) break;      // every key in this bin is taken: the prefix is the threshold
-        __syncthreads();
+        krem -= above;
+        if (bc == krem) break;               // every key in this bin is taken: the prefix is the threshold
     }
-    const uint64_t T = prefix;          // keys >= T are exactly the K best (low bits of T are zero past the stop)
+    const uint64_t T = prefix;               // keys >= T are exactly the K best (low bits of T are zero past the stop)
 
     // ---- 2. how many of the ranked winners to keep -----------------------------
-    if (!use_p || nforced >= k_max) {
-        for (int j = tid; j < nkb; j += 256) keep[j] = keys[j] >= T;
-    } else {
-        mx = block_reduce(mx, red, true);
-        float z_local = 0.f;
-        for (int j = tid; j < nkb; j += 256) z_local += expf(s[j] - mx);
-        const float Z = block_reduce(z_local, red, false);
-        // compact the K winners, then sort them descending
-        if (tid == 0) n_top_s = 0;
-        for (int i = tid; i < P2K; i += 256) tops[i] = 0ull;
-        __syncthreads();
-        for (int j = tid; j < nkb; j += 256)
-            if (keys[j] >= T) tops[atomicAdd(&n_top_s, 1)] = keys[j];   // order fixed by the sort below
-        __syncthreads();
-        for (int size = 2; size <= P2K; size <<= 1) {
-            for (int stride = size >> 1; stride > 0; stride >>= 1) {
-                for (int t = tid; t < P2K / 2; t += 256) {
-                    const int lo = 2 * t - (t & (stride - 1));
-                    const int hi = lo + stride;
-                    const bool desc = (lo & size) == 0;
-                    const uint64_t a = tops[lo], b = tops[hi];
-                    if ((a < b) == desc) { tops[lo] = b; tops[hi] = a; }
-                }
-                __syncthreads();
+    uint64_t T2 = T;
+    if (top_p < 1.f && nforced < k_max) {
+        mx = wave_max(mx);
+        float z = 0.f;
+#pragma unroll
+        for (int e = 0; e < NPL; ++e)
+            if (lane + 64 * e < nkb) z += expf(score_of_key(key[e]) - mx);
+        const float Z = wave_sum(z);
+        // Softmax masses of the ranked (non-forced) candidates as fixed-point
+        // integers in units of 2^-31: their sums do not depend on the order of
+        // the additions, so the walk below is deterministic.
+        constexpr float kFix = 2147483648.f;
+#pragma unroll
+        for (int e = 0; e < NPL; ++e) {
+            wt[e] = (lane + 64 * e < nkb && !(key[e] >> 63))
+                        ? (uint32_t)(expf(score_of_key(key[e]) - mx) / Z * kFix) : 0u;
+            in[e] = wt[e] != 0u;
+        }
+        uint32_t mrem = (uint32_t)(top_p * kFix);
+        uint64_t xp = 0, xmask = 0;
+        bool reached = true;
+#pragma unroll 1
+        for (int shift = 56; shift >= 0; shift -= 8) {
+            uint32_t above = 0, bc = 0;
+            const int d = digit_step<NPL, true>(key, wt, in, xp, xmask, shift, mrem, lds, lane, above, bc);
+            if (d < 0) { reached = false; break; }   // the ranked mass never reaches top_p
+            xp |= (uint64_t)d << shift;
+            xmask |= (uint64_t)0xff << shift;
+            mrem -= above;
+            if (bc == 1) {                           // one key left in the bin: it is the crossing key
+                uint64_t x = 0;
+#pragma unroll
+                for (int e = 0; e < NPL; ++e)
+                    if (in[e] && (key[e] & xmask) == xp) x = key[e];
+                xp = wave_max_u64(x);
+                break;
             }
         }
-        if (tid == 0) {
-            // forced blocks (all of them, since nforced < k_max) lead the ranked list
-            float cum = 0.f;
-            int r = K - nforced;             // every ranked candidate that fits the cap
-            for (int i = nforced; i < K; ++i) {
-                cum += expf(score_of_key(tops[i]) - mx) / Z;
-                if (cum >= top_p) { r = i - nforced + 1; break; }
-            }
-            n_keep_s = nforced + r;
-        }
-        __syncthreads();
-        for (int i = tid; i < n_keep_s; i += 256) keep[index_of_key(tops[i])] = 1;
+        if (reached && xp > T2) T2 = xp;             // past the cap (xp < T) every winner stays
     }
-    __syncthreads();
 
     // ---- 3. ascending compaction ------------------------------------------------
-    const int lane = tid & 63, w = tid >> 6;
     int32_t* out = kv_idx + row * (int64_t)k_max;
     int base = 0;
-    for (int r0 = 0; r0 < nkb; r0 += 256) {
-        const int j = r0 + tid;
-        const bool kj = j < nkb && keep[j];
+#pragma unroll
+    for (int e = 0; e < NPL; ++e) {
+        const int j = lane + 64 * e;
+        const bool kj = j < nkb && key[e] >= T2;
         const uint64_t bal = __ballot(kj);
-        if (lane == 0) wave_tot[w] = __popcll(bal);
-        __syncthreads();
-        int before = 0, total = 0;
-        for (int i = 0; i < 4; ++i) { before += (i < w) ? (int)wave_tot[i] : 0; total += (int)wave_tot[i]; }
-        if (kj) out[base + before + __popcll(bal & ((1ull << lane) - 1ull))] = j;
-        base += total;
-        __syncthreads();
+        if (kj) out[base + __popcll(bal & lt)] = j;
+        base += __popcll(bal);
     }
-    if (tid == 0) kv_cnt[row] = base;
+    if (lane == 0) kv_cnt[row] = base;
 }
 
 }  // namespace vsa
@@ -202,11 +264,20 @@ extern "C" int vsa_select_topk(const float* scores, int B, int H, int nqb, int n
     if (!(top_p > 0.f) || !(top_p <= 1.f)) return fail(VSA_ERR_INVALID, "vsa_select_topk: top_p must be in (0, 1]");
     int64_t rows = (int64_t)B * H * nqb;
     if (rows >= (1ll << 31)) return fail(VSA_ERR_INVALID, "vsa_select_topk: too many rows");
-    int P2K = 512;                       // every thread owns whole compare pairs
-    while (P2K < k_max) P2K <<= 1;
-    if (top_p >= 1.f) P2K = 0;           // no sort without top-p
-    const size_t shm = (size_t)nkb * 8 + (size_t)P2K * 8 + (size_t)((nkb + 15) & ~15);
-    hipLaunchKernelGGL(select_kernel, dim3((unsigned)rows), dim3(256), shm, as_stream(stream), scores, nqb, nkb, P2K,
-                       forced, k_max, top_p, kv_idx, kv_cnt);
+    const int npl = (nkb + 63) / 64;
+    const dim3 grid((unsigned)rows);
+    hipStream_t st = as_stream(stream);
+#define VSA_SELECT_LAUNCH(NPL)                                                                                    \
+    hipLaunchKernelGGL(select_kernel<NPL>, grid, dim3(64), 0, st, scores, nqb, nkb, forced, k_max, top_p, kv_idx, \
+                       kv_cnt)
+    if (npl <= 4) VSA_SELECT_LAUNCH(4);
+    else if (npl <= 8) VSA_SELECT_LAUNCH(8);
+    else if (npl <= 12) VSA_SELECT_LAUNCH(12);
+    else if (npl <= 16) VSA_SELECT_LAUNCH(16);
+    else if (npl <= 24) VSA_SELECT_LAUNCH(24);
+    else if (npl <= 32) VSA_SELECT_LAUNCH(32);
+    else if (npl <= 48) VSA_SELECT_LAUNCH(48);
+    else VSA_SELECT_LAUNCH(64);
+#undef VSA_SELECT_LAUNCH
     return launch_status("vsa_select_topk");
 }
