@@ -43,9 +43,15 @@ def test_block_scores_cube_layout_blk_len():
     assert_scores_close(host(S), rS, "cube")
 
 
+# nkb spans every register width of the one-wave kernel (4 ... 64 keys per lane,
+# 4096 = the largest row); a quantum of 1000 makes every score of a row equal,
+# so the order comes from the indices alone
 @pytest.mark.parametrize("nkb,k_max,top_p,quant", [(10, 3, 1.0, 0.5), (10, 10, 0.6, None), (624, 93, 0.9, None),
                                                    (624, 93, 0.5, None), (300, 40, 1.0, 0.25), (1536, 154, 1.0, None),
-                                                   (2048, 200, 0.95, None), (1, 1, 1.0, None), (5, 2, 0.3, 1.0)])
+                                                   (2048, 200, 0.95, None), (1, 1, 1.0, None), (5, 2, 0.3, 1.0),
+                                                   (1000, 100, 0.9, None), (3000, 300, 0.8, None),
+                                                   (4096, 4096, 0.5, None), (4096, 1, 1.0, 0.25),
+                                                   (624, 93, 0.9, 1000.0), (1536, 154, 1.0, 1000.0)])
 def test_select_topk_random_rows(nkb, k_max, top_p, quant):
     announce(f"select nkb={nkb} k={k_max} p={top_p}")
     rng = np.random.default_rng(nkb + k_max)
