@@ -694,7 +694,7 @@ def extra_layers(torch, V, PL, T):
     nat_b = q.numel() * q.element_size()                         # one natural-order tensor
     cube_b = qc.numel() * qc.element_size()                      # one cube-major tensor, pad slots included
     gbs = {"a3_cube_permute_qkv": 3 * (nat_b + cube_b),          # read every token, write every slot
-           "a4_block_scores": 2 * cube_b + S.numel() * 4,        # Q and K read once, S written
+           "a4_block_scores": 2 * nat_b + S.numel() * 4,         # the valid rows of Q and K read, S written
            "a8_cube_permute_o": cube_b + nat_b}
     hbm = {key: {"GBps": round(b / (np.mean(times[key]) * 1e-3) / 1e9, 1),
                  "frac_of_hbm_peak": round(b / (np.mean(times[key]) * 1e-3) / 1e9 / PEAK_HBM_GBS, 3)}
