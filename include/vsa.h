@@ -144,8 +144,9 @@ int vsa_permute(const void* src, void* dst, int B, int H, vsa_grid g, int D, int
  *   blk_len   optional device int32 [nb]
  *   scale     > 0 (1/sqrt(D) for the attention scale)
  *   scores    out, device fp32 [B, H, nb, nb]
- *   qpool, kpool  out, device fp32 [B, H, nb, D] (required; mean vectors; a block
- *             with no valid row pools to 0). Accumulation in fp32. */
+ *   qpool, kpool  out, device fp32 [B, H, nb, D] (required, 16-byte aligned; mean
+ *             vectors; a block with no valid row pools to 0). Accumulation in fp32;
+ *             the score product runs on the fp32 matrix cores. */
 int vsa_block_scores(const void* q, const void* k, int B, int H, int N, int D, int dtype, int bs,
                      const int32_t* blk_len, float scale, float* scores, float* qpool,
                      float* kpool, void* stream);
@@ -164,7 +165,9 @@ int vsa_block_scores(const void* q, const void* k, int B, int H, int N, int D, i
  *   k_max    1 <= k_max <= nkb;  top_p in (0, 1] (1 = off)
  *   kv_idx   out, device int32 [B, H, nqb, k_max] (entries past kv_cnt unspecified)
  *   kv_cnt   out, device int32 [B, H, nqb]
- * Arithmetic in fp32 (softmax and cumulative mass), ties exact. */
+ * Softmax terms in fp32; the cumulative mass adds them as integers in units of
+ * 2^-31 (each term truncated once), so the kept count does not depend on the
+ * order of the additions. Ties exact. */
 int vsa_select_topk(const float* scores, int B, int H, int nqb, int nkb, const uint8_t* forced,
                     int k_max, float top_p, int32_t* kv_idx, int32_t* kv_cnt, void* stream);
 
