@@ -139,6 +139,9 @@ def test_scores_select_mask_validation():
     assert L.vsa_block_scores(p, p, 1, 2, 256, 128, 0, 96, None, 0.1, p, p, p, None) == V.VSA_ERR_UNSUPPORTED
     assert L.vsa_block_scores(p, p, 1, 2, 256, 128, 1, 64, None, 0.1, p, p, p, None) == V.VSA_ERR_UNSUPPORTED
     assert L.vsa_block_scores(p, p, 1, 2, 256, 128, 0, 64, None, 0.1, p, None, p, None) == V.VSA_ERR_INVALID
+    odd = ctypes.c_void_p(0x1004)                    # pooled vectors are read 16 bytes at a time
+    assert L.vsa_block_scores(p, p, 1, 2, 256, 128, 0, 64, None, 0.1, p, odd, p, None) == V.VSA_ERR_INVALID
+    assert L.vsa_block_scores(p, p, 1, 2, 256, 128, 0, 64, None, 0.1, p, p, odd, None) == V.VSA_ERR_INVALID
     assert L.vsa_select_topk(p, 1, 2, 4, 4, None, 0, 1.0, p, p, None) == V.VSA_ERR_INVALID     # k_max < 1
     assert L.vsa_select_topk(p, 1, 2, 4, 4, None, 5, 1.0, p, p, None) == V.VSA_ERR_INVALID     # k_max > nkb
     assert L.vsa_select_topk(p, 1, 2, 4, 4, None, 2, 0.0, p, p, None) == V.VSA_ERR_INVALID     # top_p <= 0
