@@ -100,21 +100,52 @@ __global__ __launch_bounds__(256) void fp8_fill_u32_kernel(uint32_t* p, int64_t 
     if (i < n) p[i] = 0u;
 }
 
-__global__ __launch_bounds__(128) void fp8_vamax_kernel(const uint16_t* x, uint32_t* amax_bits, int N, int ntile) {
-    const int64_t bh = blockIdx.x / ntile;
-    const int t = (int)(blockIdx.x - bh * ntile);
-    const int ch = threadIdx.x;
-    float am = 0.f;
-    for (int r = t * kF8Block; r < min(N, t * kF8Block + kF8Block); ++r)
-        am = fmaxf(am, fabsf(bf16_bits_to_f32(x[(bh * N + r) * 128 + ch])));
-    atomicMax(&amax_bits[bh * 128 + ch], __float_as_uint(am));
+// A workgroup per (b, h, kAmaxRows rows): 16-byte loads, 16 rows per pass, the
+// lanes' maxima folded by shuffles and LDS, then one integer max per channel.
+constexpr int kAmaxRows = 512;
+
+__global__ __launch_bounds__(256) void fp8_vamax_kernel(const uint16_t* x, uint32_t* amax_bits, int N, int nchunk) {
+    __shared__ float red[4][128];
+    const int64_t bh = blockIdx.x / nchunk;
+    const int chunk = (int)(blockIdx.x - bh * nchunk);
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int c = threadIdx.x & 15;                              // channels 8 c .. 8 c + 7
+    const int r_end = min(N, (chunk + 1) * kAmaxRows);
+    float am[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+    for (int r = chunk * kAmaxRows + (threadIdx.x >> 4); r < r_end; r += 16) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(x + (bh * N + r) * 128 + 8 * c);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            am[2 * e] = fmaxf(am[2 * e], fabsf(bf16_bits_to_f32(v[e] & 0xffffu)));
+            am[2 * e + 1] = fmaxf(am[2 * e + 1], fabsf(bf16_bits_to_f32(v[e] >> 16)));
+        }
+    }
+#pragma unroll
+    for (int off = 16; off < 64; off <<= 1)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) am[i] = fmaxf(am[i], __shfl_xor(am[i], off));
+    if (lane < 16)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) red[w][8 * c + i] = am[i];
+    __syncthreads();
+    if (threadIdx.x < 128) {
+        const float m = fmaxf(fmaxf(red[0][threadIdx.x], red[1][threadIdx.x]), fmaxf(red[2][threadIdx.x], red[3][threadIdx.x]));
+        atomicMax(&amax_bits[bh * 128 + threadIdx.x], __float_as_uint(m));
+    }
 }
 
 __global__ __launch_bounds__(256) void fp8_quant_vt_kernel(const uint16_t* x, const uint32_t* amax_bits,
                                                            uint8_t* tiles, int N, int ntile) {
     __shared__ uint8_t tile[128][kF8Block];                     // [channel][column]
+    __shared__ float inv_s[128];                                // 448 / amax per channel
     const int64_t bh = blockIdx.x / ntile;
     const int t = (int)(blockIdx.x - bh * ntile);
+    if (threadIdx.x < 128) {
+        const float am = __uint_as_float(amax_bits[bh * 128 + threadIdx.x]);
+        inv_s[threadIdx.x] = am > 0.f ? kE4M3Max / am : 0.f;
+    }
+    __syncthreads();
     // thread: key k = threadIdx.x / 4, channels 32 (threadIdx.x & 3) + [0, 32)
     const int k = threadIdx.x >> 2, c0 = 32 * (threadIdx.x & 3);
     const int row = t * kF8Block + k;
@@ -129,9 +160,7 @@ __global__ __launch_bounds__(256) void fp8_quant_vt_kernel(const uint16_t* x, co
 #pragma unroll
             for (int hh = 0; hh < 2; ++hh) {
                 const int ch = c0 + 8 * i + 2 * e + hh;
-                const float am = __uint_as_float(amax_bits[bh * 128 + ch]);
-                const float inv = am > 0.f ? kE4M3Max / am : 0.f;
-                const float y = bf16_bits_to_f32(hh ? (w[e] >> 16) : (w[e] & 0xffffu)) * inv;
+                const float y = bf16_bits_to_f32(hh ? (w[e] >> 16) : (w[e] & 0xffffu)) * inv_s[ch];
                 const int code = __builtin_amdgcn_cvt_pk_fp8_f32(clamp448(y), 0.f, 0, false) & 0xff;
                 tile[ch][col] = ok ? (uint8_t)code : (uint8_t)0;
             }
@@ -398,7 +427,8 @@ extern "C" int vsa_fp8_quantize(const void* x, int B, int H, int N, int D, int d
         uint32_t* bits = reinterpret_cast<uint32_t*>(scales);
         const int64_t n = BH * 128;
         hipLaunchKernelGGL(fp8_fill_u32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, bits, n);
-        hipLaunchKernelGGL(fp8_vamax_kernel, dim3((unsigned)(BH * ntile)), dim3(128), 0, s, xb, bits, N, (int)ntile);
+        const int64_t nchunk = (N + kAmaxRows - 1) / kAmaxRows;
+        hipLaunchKernelGGL(fp8_vamax_kernel, dim3((unsigned)(BH * nchunk)), dim3(256), 0, s, xb, bits, N, (int)nchunk);
         hipLaunchKernelGGL(fp8_quant_vt_kernel, dim3((unsigned)(BH * ntile)), dim3(256), 0, s, xb, bits, out, N,
                            (int)ntile);
         hipLaunchKernelGGL(fp8_vscale_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, bits, scales, n);
