@@ -747,8 +747,8 @@ def extra_layers(torch, V, PL, T):
     w = WAN480_SEMANTIC
     q, k, v = (torch.from_numpy(x).to(torch.bfloat16).to(dev) for x in make_qkv(w))
     Cq, Ck, iters, top_p = w.extra["Cq"], w.extra["Ck"], w.extra["iters"], w.extra["top_p"]
-    times = {}
-    for rep in range(4):
+    times, reps = {}, []
+    for rep in range(4):                     # queued ahead, one sync at the end
         e = [T.ev()]
         cq, lq, nq = V.vsa_kmeans(q, Cq, iters)
         e.append(T.ev())
@@ -768,11 +768,13 @@ def extra_layers(torch, V, PL, T):
         e.append(T.ev())
         o = V.vsa_gather_rows(os_, pq, inverse=True)
         e.append(T.ev())
-        torch.cuda.synchronize()
         if rep:
-            for key, i in (("kmeans_q", 0), ("kmeans_k", 1), ("cluster_order_qk", 2), ("gather_qkv", 3),
-                           ("scores_select", 4), ("varlen_attention", 5), ("gather_o", 6)):
-                times.setdefault(key, []).append(e[i].elapsed_time(e[i + 1]))
+            reps.append(e)
+    torch.cuda.synchronize()
+    for e in reps:
+        for key, i in (("kmeans_q", 0), ("kmeans_k", 1), ("cluster_order_qk", 2), ("gather_qkv", 3),
+                       ("scores_select", 4), ("varlen_attention", 5), ("gather_o", 6)):
+            times.setdefault(key, []).append(e[i].elapsed_time(e[i + 1]))
     nqh, nkh, ih, ch = (x.cpu().numpy().astype(np.int64) for x in (nq, nk, idx, cnt))
     kept = 0.0
     for h in range(w.H):

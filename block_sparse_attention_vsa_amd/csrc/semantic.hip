@@ -147,10 +147,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
 // ---- update: one workgroup per (bh, cluster) over its members ------------------
 // The members of cluster c are positions [off[c], off[c + 1]) of the stable
 // cluster-major order of the current labels. 32 streams (4 per wave, 16 lanes x
-// 8 channels each) take every 32nd member, the streams' partial sums are added
-// in stream order: a fixed order, independent of scheduling.
+// 8 channels each) take every 32nd member, 16 members per stream and pass; the
+// streams' partial sums are added in stream order: a fixed order, independent
+// of scheduling.
 __global__ __launch_bounds__(512) void km_update_kernel(KmArgs a, const int32_t* perm, const int32_t* off) {
-    constexpr int STREAMS = 32, UNROLL = 8;
+    constexpr int STREAMS = 32, UNROLL = 16;
     __shared__ float part[STREAMS][kKmD];
     __shared__ float mb[kKmD];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -165,10 +166,20 @@ __global__ __launch_bounds__(512) void km_update_kernel(KmArgs a, const int32_t*
     float acc[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+    // the member indices of the next pass are loaded before this pass's rows, so
+    // a large cluster waits on one load latency per pass instead of two
+    int tok_next[UNROLL];
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) tok_next[u] = m0 + stream < m1 ? ph[min(m0 + stream + STREAMS * u, m1 - 1)] : 0;
     for (int p0 = m0 + stream; p0 < m1; p0 += STREAMS * UNROLL) {
         int tok[UNROLL];
 #pragma unroll
-        for (int u = 0; u < UNROLL; ++u) tok[u] = ph[min(p0 + STREAMS * u, m1 - 1)];
+        for (int u = 0; u < UNROLL; ++u) tok[u] = tok_next[u];
+        const int pn = p0 + STREAMS * UNROLL;
+        if (pn < m1) {
+#pragma unroll
+            for (int u = 0; u < UNROLL; ++u) tok_next[u] = ph[min(pn + STREAMS * u, m1 - 1)];
+        }
         u32x4 row[UNROLL];
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u)
