@@ -35,13 +35,17 @@ def quantised(q, k, v):
     return q8, k8, vt, qs, ks, vs                         # the binding's argument order
 
 
-@pytest.mark.parametrize("N,amp", [(1000, 1.0), (777, 30.0), (64, 1.0), (1, 1.0), (200, 1e-3)])
+# 3000 and 2049 span several 512-row amax chunks of V with a ragged last one
+@pytest.mark.parametrize("N,amp", [(1000, 1.0), (777, 30.0), (64, 1.0), (1, 1.0), (200, 1e-3), (3000, 1.0),
+                                   (2049, 5.0)])
 def test_quantise_bit_exact(N, amp):
     announce(f"fp8 quantise N={N} amp={amp}")
     g = np.random.default_rng(N)
     x = bf16_values(amp * g.standard_normal((1, 2, N, 128)) * np.exp(g.standard_normal((1, 2, N, 1))))
     if N >= 128:
         x[0, 1, 64:128] = 0.0                                  # a zero block
+    if N > 2048:
+        x[0, 0, N - 1, 5] = 4.0 * np.abs(x[0, 0, :, 5]).max()  # a channel's maximum in the last row
     xd = dev(x)
     c, s = (host(t) for t in V.vsa_fp8_quantize(xd, V.VSA_FP8_ROWS))
     rc, rs = OF.quantise_rows(x)
