@@ -210,8 +210,9 @@ __global__ __launch_bounds__(64) void select_kernel(const float* __restrict__ sc
         constexpr float kFix = 2147483648.f;
 #pragma unroll
         for (int e = 0; e < NPL; ++e) {
-            wt[e] = (lane + 64 * e < nkb && !(key[e] >> 63))
-                        ? (uint32_t)(expf(score_of_key(key[e]) - mx) / Z * kFix) : 0u;
+            const float pm = expf(score_of_key(key[e]) - mx) / Z * kFix;
+            // a NaN mass (a row of -inf or NaN scores) weighs nothing
+            wt[e] = (lane + 64 * e < nkb && !(key[e] >> 63) && pm > 0.f) ? (uint32_t)fminf(pm, kFix) : 0u;
             in[e] = wt[e] != 0u;
         }
         uint32_t mrem = (uint32_t)(top_p * kFix);
