@@ -4,7 +4,8 @@
 // Sparse Video-Gen page, "Approach": a token-major to frame-major layout
 // transformation makes the same-position tokens of all frames contiguous, so a
 // temporal head's sparse pattern becomes dense tiles. USV page, Figure 2
-// caption: queries, keys and values are partitioned into local 3D cubes.
+// caption: the cube layout groups the tokens of Q, K and V into 4x4x4
+// spatio-temporal cubes, each stored as one 64-slot block.
 //
 // Pure data movement, HBM-bound: every destination row (one token's D values)
 // is produced by one group of lanes moving 16 bytes each, so a row of a bf16

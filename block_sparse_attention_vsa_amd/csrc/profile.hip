@@ -19,9 +19,9 @@
 //     sub-tile ahead. Per sub-tile: S^T once on MFMA, the dense online softmax
 //     (lazy running offset), and P V for the dense set. A candidate reuses the
 //     dense probabilities with its unkept keys zeroed (the same running offset
-//     serves every set), and its softmax and P V are skipped outright when
-//     none of the wave's rows keeps a key of the sub-tile. Each (slot, row,
-//     split) writes a partial record (m, l, O).
+//     serves every set); its P V products run on every sub-tile, with P zero
+//     where the candidate keeps nothing. Each (slot, row, split) writes a
+//     partial record (m, l, O).
 //  3. merge: one workgroup per (b, h, sampled row) combines the partial records
 //     in split order (exact log-sum-exp rescaling), normalises every slot and
 //     sums each candidate's squared difference to the dense output.

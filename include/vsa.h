@@ -98,8 +98,8 @@ int vsa_version(void);
 int vsa_selftest_host(void);
 
 /* Number of 4x4x4 cubes of a grid and padded slot count (= 64 * cubes). Host only.
- * Cubes: USV page, Figure 2 caption (queries, keys and values partitioned into
- * local 3D cubes). */
+ * Cubes: USV page, Figure 2 caption (the tokens of Q, K and V grouped into small
+ * spatio-temporal cubes). */
 int vsa_cube_dims(vsa_grid g, int32_t* n_cubes, int32_t* n_slots);
 
 /* Any-rule block mask of a token pattern.

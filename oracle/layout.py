@@ -8,8 +8,8 @@ Natural order lists tokens frame by frame, row by row: position n holds the toke
   all frames of one spatial position (y, x) sit next to each other, ordered by t,
   and positions follow raster order of (y, x). The oracle builds it by sorting
   tokens on the key (y, x, t), not from a closed-form index map.
-* Cube order (USV page, Figure 2 caption: queries, keys and values are partitioned
-  into local 3D cubes): cubes of c x c x c tokens in raster order of their
+* Cube order (USV page, Figure 2 caption: the tokens of Q, K and V grouped into
+  small spatio-temporal cubes): cubes of c x c x c tokens in raster order of their
   (t/c, y/c, x/c) index, each owning c^3 slots; a cube's valid tokens fill its
   first slots in (t, y, x) raster order and the rest are zero padding. The oracle
   builds it by a stable sort of tokens on their cube id.

@@ -62,27 +62,3 @@ def select(scores, forced=None, k_max: int = 1, top_p: float = 1.0):
             cnt[u, qb] = kept.size
     return idx.reshape(s.shape[:-1] + (k_max,)), cnt.reshape(s.shape[:-1])
 
-
-def boundary_gap(scores, forced, k_max, top_p, kept: np.ndarray):
-    """Diagnostics for comparing a selection made in lower precision.
-
-    Returns (boundary_score, cum_at_boundary): the score of the last kept
-    non-forced candidate in rank order, and the cumulative top-p mass there
-    (None when top-p is off). A block whose score lies within a small gap of
-    boundary_score may legitimately flip in a lower-precision selection.
-    """
-    s = np.asarray(scores, np.float64)
-    f = np.zeros(s.size, bool) if forced is None else (np.asarray(forced) != 0)
-    rank = np.argsort(-s, kind="stable")
-    cand = rank[~f[rank]]
-    kept_c = [j for j in cand if j in set(kept.tolist())]
-    if not kept_c:
-        return None, None
-    last = kept_c[-1]
-    bscore = s[last]
-    if top_p < 1.0:
-        e = np.exp(s - s.max())
-        p = e / e.sum()
-        c = np.cumsum(p[cand])
-        return bscore, float(c[len(kept_c) - 1])
-    return bscore, None

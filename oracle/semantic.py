@@ -9,12 +9,11 @@ gives no further detail; the plainest reading, used here:
 * k-means (Lloyd's algorithm) per (b, h), separately on the queries (Cq clusters)
   and on the keys (Ck clusters; values follow the keys). Seeds: the tokens at
   positions floor(c N / C). One iteration assigns every token to its nearest
-  centroid and then replaces each centroid by the mean of its members (a cluster
-  left empty keeps its centroid). The centroids take part in the distance in
-  bf16 (the precision of the tokens): token x goes to
-  argmin_c ( ||m_c||^2 - 2 <x, m_c> ),  m_c = bf16(centroid c),
-  ties to the lower index. After the last iteration the returned centroids are
-  the means of the returned assignment.
+  centroid in squared Euclidean distance, argmin_c ||x - m_c||^2 with the exact
+  (fp64) centroids, ties to the lower index, and then replaces each centroid by
+  the mean of its members (a cluster left empty keeps its centroid). After the
+  last iteration the returned centroids are the means of the returned
+  assignment.
 * Cluster-major order: a stable sort of the tokens by cluster (members of a
   cluster keep their natural order); cluster c occupies the positions
   [off_c, off_c + n_c), off the exclusive prefix sum of the sizes n.
@@ -37,21 +36,14 @@ from .attention import masked_attention
 from .select import select
 
 
-def _bf16(x: np.ndarray) -> np.ndarray:
-    """Round to bfloat16 (nearest, ties to even) and return as float64."""
-    f = np.ascontiguousarray(x, dtype=np.float32)
-    u = f.view(np.uint32).astype(np.uint64)
-    lsb = (u >> 16) & 1
-    r = ((u + 0x7FFF + lsb) >> 16) << 16
-    return r.astype(np.uint32).view(np.float32).astype(np.float64)
-
-
 def assign(x: np.ndarray, centroids: np.ndarray) -> np.ndarray:
-    """Nearest centroid of every row of x [N, D] (centroids [C, D] rounded to bf16)."""
+    """Nearest centroid of every row of x [N, D]: argmin_c ||x - m_c||^2 in fp64,
+    the first minimum (lower index) on a tie. The squared distance is expanded as
+    ||x||^2 + ||m_c||^2 - 2 <x, m_c> so that one matrix product serves all pairs."""
     x = np.asarray(x, np.float64)
-    m = _bf16(centroids)
-    d = (m * m).sum(axis=1)[None, :] - 2.0 * (x @ m.T)
-    return np.argmin(d, axis=1)                         # first minimum: the lower index
+    m = np.asarray(centroids, np.float64)
+    d = (x * x).sum(axis=1)[:, None] + (m * m).sum(axis=1)[None, :] - 2.0 * (x @ m.T)
+    return np.argmin(d, axis=1)
 
 
 def update(x: np.ndarray, labels: np.ndarray, centroids: np.ndarray):

@@ -159,3 +159,33 @@ def test_bwd_cube_wan_full_shape_sampled():
     valid = np.arange(n_slots) % 64 < counts[np.arange(n_slots) // 64]
     for t in (dq, dk, dv):
         assert (t[:, :, ~valid] == 0).all()
+
+
+def test_bwd_spatial_wan_full_shape_sampled():
+    """The Wan 480p backward as the benchmark times it (12 heads, N = 32760,
+    bs 128, the spatial w=1 block mask on every head, 256 key blocks with a
+    ragged last block of 120 keys): dQ at sampled query rows and dK, dV at
+    sampled key rows (first, middle and ragged last key block) of two heads
+    against the oracle; mask and list forms bit-identical."""
+    from workloads import WAN480
+    w = WAN480
+    announce("attn bwd spatial wan full shape")
+    q, k, v = make_qkv(w)
+    do = to_bf16_values(rng(w.seed, 40).standard_normal(q.shape).astype(np.float32))
+    td = [dev(x) for x in (q, k, v, do)]
+    m = OM.pattern_mask(w.grid, w.bs, "spatial", 1)
+    mask = np.broadcast_to(m, (1, w.H, w.nb, w.nb)).copy()
+    g = run(td, w.bs, mask=dev_u8(mask))
+    idx, cnt = OM.mask_to_list(mask)
+    gl = run(td, w.bs, idx=dev_i32(idx), cnt=dev_i32(cnt))
+    for a, b in zip(g, gl):
+        assert torch.equal(a, b)
+    heads = [0, 11]
+    r = rng(4, 41)
+    q_rows = np.unique(np.concatenate([[0, 127], r.choice(w.N, 40, replace=False), [w.N - 120, w.N - 1]]))
+    k_rows = np.array([3, 128 * 131 + 77, w.N - 119, w.N - 1])
+    ref = OB.block_sparse_attention_bwd_rows(*(x[:, heads] for x in (q, k, v, do)), m, w.bs, q_rows, k_rows)
+    dq, dk, dv = (host(t[:, heads]) for t in g)
+    assert_grad_close(dq[:, :, q_rows], ref[0], "wan spatial dq")
+    assert_grad_close(dk[:, :, k_rows], ref[1], "wan spatial dk")
+    assert_grad_close(dv[:, :, k_rows], ref[2], "wan spatial dv")

@@ -18,19 +18,22 @@ from workloads import WAN480, WAN480_CUBE, LONG126, make_qkv, profile_rows, samp
 
 pytestmark = pytest.mark.gpu
 
-ERR_REL = 1e-2      # relative error allowed on each candidate's profile error
+ERR_REL = 1e-3      # relative error allowed on each candidate's profile error
+GAP_MIN = 1e-4      # choices must agree wherever the oracle's relative gap reaches this
 
 
 def check_profile(err_g, ch_g, err_r, ch_r, what):
     rel = np.abs(err_g - err_r) / np.maximum(np.abs(err_r), 1e-30)
     assert rel.max() <= ERR_REL, f"{what}: profile error off by {rel.max():.2e} (relative)"
-    # a choice may differ only where the oracle's own gap is within twice that bound
+    # each candidate's error is off by at most rel.max() relative, so a relative gap
+    # above twice that cannot reorder the two smallest errors
     e = np.sort(err_r, axis=-1)
     gap = (e[..., 1] - e[..., 0]) / np.maximum(e[..., 1], 1e-30) if err_r.shape[-1] > 1 else np.ones(ch_r.shape)
-    clear = gap > 2 * ERR_REL
+    clear = gap >= max(GAP_MIN, 2 * rel.max())
     assert np.array_equal(ch_g[clear], ch_r[clear]), f"{what}: choice differs where the gap is clear"
     print(f"[{what}] max rel err {rel.max():.2e}, choices {ch_g.ravel().tolist()} vs oracle {ch_r.ravel().tolist()}, "
-          f"min gap {gap.min():.2e}")
+          f"min gap {gap.min():.2e}, unchecked {int((~clear).sum())}")
+    return gap
 
 
 def small(grid, H, amplitude, seed, bs=64):
@@ -72,18 +75,28 @@ def test_profile_candidate_counts_and_identical_candidates(P):
         assert np.array_equal(ge[..., 1], ge[..., 3])      # identical candidates, identical errors
 
 
-def test_profile_wan_full_shape():
+@pytest.mark.parametrize("amplitude", [0.5, 4.0])
+def test_profile_wan_full_shape(amplitude):
     """The benchmarked launch: Wan 480p, 12 heads, 1 % rows (328), spatial w=1 in
-    natural order vs temporal w=0 in frame-major order."""
-    w = WAN480
-    announce("profile wan full")
+    natural order vs temporal w=0 in frame-major order. At amplitude 0.5 (the
+    benchmark's generator) every head prefers the spatial pattern; at 4.0 the
+    planted head types show (even heads spatial, odd heads temporal), so the
+    choice is mixed and both outcomes are checked against the oracle at the full
+    shape."""
+    w = WAN480.scaled(name=f"wan480_amp{amplitude}", amplitude=amplitude)
+    announce(f"profile wan full amp={amplitude}")
     q, k, v = make_qkv(w)
     rows = profile_rows(w)
     assert rows.size == 328
     cands = np.stack([OM.pattern_mask(w.grid, w.bs, "spatial", 1), OM.pattern_mask(w.grid, w.bs, "temporal", 0)])
     err, ch = V.vsa_profile_heads(dev(q), dev(k), dev(v), w.grid, w.bs, dev_i32(rows), dev_u8(cands), [0, 1])
     er, cr = OPR.profile_heads(q, k, v, w.grid, w.bs, rows, cands, [0, 1])
-    check_profile(host(err), host(ch), er, cr, "wan full")
+    gap = check_profile(host(err), host(ch), er, cr, f"wan full amp {amplitude}")
+    if amplitude == 4.0:
+        from workloads import planted_head_type
+        assert np.array_equal(cr[0], planted_head_type(w.H)), "the oracle's choice follows the planted types"
+        assert (gap >= GAP_MIN).all()
+        assert np.array_equal(host(ch), cr)
 
 
 def test_svg_pipeline_wan_full_shape():

@@ -8,6 +8,12 @@ import torch
 
 from oracle import attention as OA
 from oracle import semantic as OS
+from workloads import to_bf16_values
+
+
+def bf16(x):
+    """Values rounded to bf16, held in fp64."""
+    return to_bf16_values(x).astype(np.float64)
 
 
 def blobs(N, C, D, seed, spread=0.05):
@@ -40,26 +46,40 @@ def test_kmeans_empty_cluster_keeps_centroid_and_ties_go_low():
     assert cent[0, 0] == 3.0 and cent[1, 0] == 0.0
 
 
-def test_kmeans_one_iteration_matches_scikit_learn():
-    """Generic data: the seeds are tokens (exact in bf16), so the first assignment
-    is the exact nearest seed in both; after one iteration the centroids equal
-    scikit-learn's Lloyd step, and its final labels (one more assignment in fp64)
-    equal this oracle's assignment to those centroids wherever the nearest two
-    centroids are further apart than the bf16 rounding of the centroids can move."""
+@pytest.mark.parametrize("iters", [1, 2, 4])
+def test_kmeans_matches_scikit_learn_on_generic_data(iters):
+    """Generic data, the same seeds: after `iters` Lloyd iterations the centroids
+    equal scikit-learn's, and its final labels (one more assignment, in fp64)
+    equal this oracle's assignment to those centroids outright, for every token."""
     from sklearn.cluster import KMeans
     g = np.random.default_rng(1)
-    x = OS._bf16(g.standard_normal((500, 16)))
+    x = bf16(g.standard_normal((500, 16)))
     C = 12
     seeds = x[(np.arange(C) * len(x)) // C]
-    cent, lab, cnt = OS.kmeans(x, C, 1)
+    cent, lab, cnt = OS.kmeans(x, C, iters)
     assert (cnt > 0).all()                                   # (scikit-learn relocates empty clusters)
-    km = KMeans(n_clusters=C, init=seeds, n_init=1, max_iter=1, tol=0.0, algorithm="lloyd").fit(x)
+    km = KMeans(n_clusters=C, init=seeds, n_init=1, max_iter=iters, tol=0.0, algorithm="lloyd").fit(x)
     np.testing.assert_allclose(km.cluster_centers_, cent, atol=1e-12)
-    d = ((x[:, None, :] - cent[None]) ** 2).sum(-1)
-    two = np.sort(d, axis=1)[:, :2]
-    clear = (two[:, 1] - two[:, 0]) > 0.1
-    assert clear.mean() > 0.8
-    np.testing.assert_array_equal(km.labels_[clear], OS.assign(x, cent)[clear])
+    np.testing.assert_array_equal(km.labels_, OS.assign(x, cent))
+
+
+def test_assign_is_nearest_centroid_by_brute_force():
+    """The assignment equals a scalar loop over every (token, centroid) pair of
+    squared Euclidean distances, the first minimum winning; duplicated centroids
+    send their tokens to the lower index."""
+    g = np.random.default_rng(9)
+    x = g.standard_normal((60, 5))
+    m = g.standard_normal((7, 5))
+    m[5] = m[2]                                              # a duplicate: index 2 must win
+    got = OS.assign(x, m)
+    for i in range(len(x)):
+        best, bd = 0, None
+        for c in range(len(m)):
+            d = sum((x[i, j] - m[c, j]) ** 2 for j in range(5))
+            if bd is None or d < bd:
+                best, bd = c, d
+        assert got[i] == best
+    assert 5 not in got.tolist()
 
 
 def test_kmeans_converges_like_scikit_learn_on_sorted_blobs():
@@ -69,7 +89,7 @@ def test_kmeans_converges_like_scikit_learn_on_sorted_blobs():
     C, per, D = 6, 90, 24
     g = np.random.default_rng(2)
     centers = 3.0 * g.standard_normal((C, D))
-    x = OS._bf16(np.repeat(centers, per, axis=0) + 0.3 * g.standard_normal((C * per, D)))
+    x = bf16(np.repeat(centers, per, axis=0) + 0.3 * g.standard_normal((C * per, D)))
     seeds = x[(np.arange(C) * len(x)) // C]
     cent, lab, _ = OS.kmeans(x, C, 5)
     km = KMeans(n_clusters=C, init=seeds, n_init=1, max_iter=5, tol=0.0, algorithm="lloyd").fit(x)
@@ -81,7 +101,7 @@ def test_kmeans_converges_like_scikit_learn_on_sorted_blobs():
 
 def test_kmeans_recovers_planted_blobs():
     x, truth = blobs(800, 6, 32, 2, spread=0.02)
-    _, lab, _ = OS.kmeans(OS._bf16(x), 12, 8)
+    _, lab, _ = OS.kmeans(bf16(x), 12, 8)
     # every found cluster lies inside one planted blob
     for c in np.unique(lab):
         assert np.unique(truth[lab == c]).size == 1
