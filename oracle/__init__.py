@@ -16,10 +16,14 @@ eye against the pages' description of the method:
 * ``select``    forced + top-k / top-p block selection
 * ``profile``   per-head pattern choice from a sample of query rows
 * ``pipeline``  the three end-to-end flows, in natural token coordinates
+* ``semantic``  k-means clustering, cluster-major order and size-weighted top-p
+* ``attention_bwd`` gradients of masked attention
+* ``fp8``       the e4m3 codec, quantisers and attention on quantised inputs
+* ``skiparse``  the Skiparse-2D token-wise and group-wise spatial patterns
 
 Pins (see tests/test_oracle_*.py) tie every function to something other than
 itself: a library special case, closed forms, invariants, hand-worked values,
 or brute force on tiny inputs. Functions without such a pin say so in their
 docstring ("parity unpinned").
 """
-from . import layout, masks, attention, scores, select, profile, pipeline  # noqa: F401
+from . import layout, masks, attention, scores, select, profile, pipeline, skiparse  # noqa: F401
