@@ -30,30 +30,51 @@ def rand_bf16(shape, seed, scale=1.0):
     return bf16(scale * np.random.default_rng(seed).standard_normal(shape))
 
 
-def decided_assignment(x, cent, rounded=True):
-    """Tokens whose nearest centroid no bf16 rounding of the centroids can change.
+def decided_assignment(x, cent, mode):
+    """Reference labels of x for centroids `cent` and the tokens whose label a
+    correct kernel cannot get wrong. The kernel ranks centroids by
+    ||m~||^2 - 2 <x, m~>, m~ = bf16(m) (round to nearest even), with fp32 sums;
+    the fp32 accumulation moves a score by at most 2^-16 (sum m~^2 + 2 sum |x m~|).
 
-    The kernel ranks centroids by ||m~||^2 - 2 <x, m~> with m~ = bf16(m) and fp32
-    sums. |m~_i - m_i| <= 2^-8 |m_i| (8 significant bits, round to nearest), so
-    the score moves from the exact ||m||^2 - 2 <x, m> by at most
-    2^-8 (2 + 2^-8) sum m_i^2 + 2^-7 sum |x_i| |m_i|, plus fp32 accumulation
-    error, bounded here by 2^-16 (sum m~^2 + 2 sum |x m~|). With rounded = False
-    (centroids that are bf16 values already, e.g. the seeds) only the fp32 term
-    applies. Returns (oracle labels, mask of tokens whose best centroid beats
-    every other by more than both bounds)."""
+    mode "seed":   the centroids are bf16 values already (the seeds); reference =
+                   the oracle's fp64 assignment; only the fp32 term applies.
+    mode "worst":  reference = the oracle's fp64 assignment to the exact centroids;
+                   |m~_i - m_i| <= 2^-8 |m_i| (8 significant bits), so rounding can
+                   move a score by at most 2^-8 (2 + 2^-8) sum m_i^2 + 2^-7 sum |x_i| |m_i|,
+                   added to the fp32 term.
+    mode "kernel": the decision taken in the kernel's precision: reference = the
+                   fp64 argmin with the centroids rounded to bf16 as the kernel
+                   rounds them; only the fp32 term applies.
+    Returns (reference labels, mask of tokens whose reference centroid beats every
+    other by more than the bounds of both)."""
     x = np.asarray(x, np.float64)
     m = np.asarray(cent, np.float64)
+    if mode == "kernel":
+        m = bf16(m)
     ref = OS.assign(x, m)
     n2 = (m * m).sum(1)
     xm = np.abs(x) @ np.abs(m).T
     bound = 2.0 ** -16 * (n2[None, :] + 2.0 * xm)
-    if rounded:
+    if mode == "worst":
         bound = bound + 2.0 ** -8 * (2.0 + 2.0 ** -8) * n2[None, :] + 2.0 ** -7 * xm
     d = n2[None, :] - 2.0 * (x @ m.T)
     r = np.arange(len(x))
     slack = d - d[r, ref][:, None] - bound - bound[r, ref][:, None]
     slack[r, ref] = np.inf
     return ref, slack.min(1) > 0
+
+
+def check_iteration(lab, x, start, t, what):
+    """Labels of iteration t, started from centroids `start`: equal to the
+    plain oracle wherever no bf16 rounding of the centroids can flip them, and
+    equal to the decision in the kernel's precision wherever fp32 sums cannot."""
+    modes = (("seed", 0.99),) if t == 1 else (("worst", 0.7), ("kernel", 0.995))
+    for mode, least in modes:
+        ref, ok = decided_assignment(x, start, mode)
+        frac = ok.mean()
+        print(f"{what} t={t} {mode}: decided {frac:.4f}, agree {(lab == ref).mean():.4f}")
+        assert frac > least, f"{what} t={t} {mode}: decided {frac:.4f}"
+        assert (lab[ok] == ref[ok]).all(), f"{what} t={t} {mode}"
 
 
 def check_kmeans_properties(x, cent, lab, cnt, C, what):
@@ -82,18 +103,16 @@ def test_kmeans_first_iteration(N, C):
     cent, lab, cnt = (host(t) for t in V.vsa_kmeans(dev(x), C, 1))
     check_kmeans_properties(x, cent, lab, cnt, C, f"N={N} C={C}")
     for h in range(2):
-        seeds = x[0, h][(np.arange(C) * N) // C]
-        ref, ok = decided_assignment(x[0, h], seeds, rounded=False)
-        assert ok.mean() > 0.99
-        assert (lab[0, h][ok] == ref[ok]).all()
+        check_iteration(lab[0, h], x[0, h], x[0, h][(np.arange(C) * N) // C], 1, f"N={N} C={C} h={h}")
 
 
 @pytest.mark.parametrize("C,iters", [(37, 3), (200, 2)])
 def test_kmeans_each_iteration_against_the_oracle_step(C, iters):
     """Iteration t of the GPU k-means starts from the centroids a (t - 1)-iteration
     run returns (the seeds for t = 1); its labels equal the oracle's fp64
-    assignment to those centroids wherever the bf16 rounding of the centroids
-    cannot change the nearest one."""
+    assignment to those centroids wherever no bf16 rounding of the centroids can
+    change the nearest one, and the decision taken in the kernel's precision
+    wherever fp32 sums cannot."""
     announce(f"kmeans per-iteration C={C} iters={iters}")
     N = 3000
     x = rand_bf16((1, 2, N, 128), 77 + C)
@@ -103,9 +122,7 @@ def test_kmeans_each_iteration_against_the_oracle_step(C, iters):
         cent, lab, cnt = (host(tt) for tt in V.vsa_kmeans(xd, C, t))
         check_kmeans_properties(x, cent, lab, cnt, C, f"t={t}")
         for h in range(2):
-            ref, ok = decided_assignment(x[0, h], prev[0, h], rounded=t > 1)
-            assert ok.mean() > 0.9, f"t={t} h={h}: decided {ok.mean():.3f}"
-            assert (lab[0, h][ok] == ref[ok]).all(), f"t={t} h={h}"
+            check_iteration(lab[0, h], x[0, h], prev[0, h], t, f"C={C} h={h}")
         prev = cent
 
 
@@ -303,8 +320,9 @@ def test_kmeans_full_semantic_shape(which):
     """k-means at the full shape (12 heads, 32760 tokens; 128 query or 256 key
     clusters, 3 iterations): the properties on every head, and on two heads each
     iteration against the oracle's fp64 assignment to the centroids the GPU
-    started that iteration from, equal wherever bf16 rounding of the centroids
-    cannot change the nearest one."""
+    started that iteration from (equal wherever no bf16 rounding of the
+    centroids can change the nearest one) and against the same decision taken in
+    the kernel's precision (equal wherever fp32 sums cannot change it)."""
     w = WAN480_SEMANTIC
     announce(f"kmeans full semantic shape {which}")
     q, k, v = make_qkv(w)
@@ -322,11 +340,7 @@ def test_kmeans_full_semantic_shape(which):
         if t == it:
             assert (l_t == lab).all() and (c_t == cent).all()      # deterministic
         for h in heads:
-            ref, ok = decided_assignment(x[0, h], prev[h], rounded=t > 1)
-            frac = ok.mean()
-            print(f"{which} t={t} head {h}: decided {frac:.4f}, agree {(l_t[0, h] == ref).mean():.4f}")
-            assert frac > 0.9, f"t={t} head {h}: decided {frac:.4f}"
-            assert (l_t[0, h][ok] == ref[ok]).all(), f"t={t} head {h}"
+            check_iteration(l_t[0, h], x[0, h], prev[h], t, f"{which} head {h}")
             prev[h] = c_t[0, h]
 
 
