@@ -54,6 +54,9 @@ _SIGNATURES = {
     "vsa_profile_workspace_bytes": (_SZ, [_I, _I, vsa_grid, _I, _I, _I]),
     "vsa_profile_heads": (_I, [_P, _P, _P, _I, _I, vsa_grid, _I, _I, _I, _P, _I, _P, _P, _I, _F,
                                _P, _P, _P, _SZ, _P]),
+    "vsa_profile_scratch_capacity": (_SZ, []),
+    "vsa_profile_heads_noalloc": (_I, [_P, _P, _P, _I, _I, vsa_grid, _I, _I, _I, _P, _I, _P, _P, _I, _F,
+                                       _P, _P, _P]),
     "vsa_mask_to_list": (_I, [_P, _I, _I, _I, _I, _P, _I, _I, _P, _P, _P]),
     "vsa_attn_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I]),
     "vsa_block_sparse_attn_fwd": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P,
@@ -383,6 +386,24 @@ def vsa_profile_heads(q, k, v, grid, bs: int, rows, cand_masks, cand_layout, sca
                                    _ptr(cand_masks), ctypes.cast(lay, ctypes.c_void_p), P, scale, _ptr(err),
                                    _ptr(choice), _ptr(workspace), workspace.numel(), _stream(q.device)),
            "vsa_profile_heads")
+    return err, choice
+
+
+def vsa_profile_scratch_capacity() -> int:
+    return lib().vsa_profile_scratch_capacity()
+
+
+def vsa_profile_heads_noalloc(q, k, v, grid, bs: int, rows, cand_masks, cand_layout, scale=None, out=None):
+    """vsa_profile_heads with the library's static scratch instead of a
+    workspace; pass `out` = (err [B, H, P] fp32, choice [B, H] int32) to make the
+    call allocate nothing at all."""
+    B, H, N, D, P, R, err, choice, lay = _profile_args(q, k, v, grid, bs, rows, cand_masks, cand_layout, out)
+    scale = default_scale(D) if scale is None else scale
+    _on_device(q, k=k, v=v, rows=rows, cand_masks=cand_masks, err=err, choice=choice)
+    _check(lib().vsa_profile_heads_noalloc(_ptr(q), _ptr(k), _ptr(v), B, H, _grid(grid), D, _dtype_code(q), bs,
+                                           _ptr(rows), R, _ptr(cand_masks), ctypes.cast(lay, ctypes.c_void_p), P,
+                                           scale, _ptr(err), _ptr(choice), _stream(q.device)),
+           "vsa_profile_heads_noalloc")
     return err, choice
 
 

@@ -30,6 +30,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "mfma_tile.h"
 
@@ -524,34 +525,42 @@ extern "C" size_t vsa_profile_workspace_bytes(int B, int H, vsa_grid g, int D, i
     return prof_plan(B, H, (int64_t)g.T * g.Hh * g.W, D, R, P).total;
 }
 
-extern "C" int vsa_profile_heads(const void* q, const void* k, const void* v, int B, int H, vsa_grid g, int D,
-                                 int dtype, int bs, const int32_t* rows, int R, const uint8_t* cand_masks,
-                                 const int32_t* cand_layout, int P, float scale, float* err, int32_t* choice,
-                                 void* workspace, size_t ws_bytes, void* stream) {
+namespace {
+
+// Host-side checks shared by both entry points; fills the plan.
+int profile_check(const char* fn, const void* q, const void* k, const void* v, int B, int H, vsa_grid g, int D,
+                  int dtype, int bs, const int32_t* rows, int R, const uint8_t* cand_masks,
+                  const int32_t* cand_layout, int P, float scale, const float* err, const int32_t* choice,
+                  ProfPlan& pl) {
     if (!q || !k || !v || !rows || !cand_masks || !cand_layout || !err || !choice)
-        return fail(VSA_ERR_INVALID, "vsa_profile_heads: null pointer");
-    if (!aligned16(q) || !aligned16(k) || !aligned16(v)) return fail(VSA_ERR_INVALID, "vsa_profile_heads: q, k, v must be 16-byte aligned");
-    if (B <= 0 || H <= 0 || g.T <= 0 || g.Hh <= 0 || g.W <= 0) return fail(VSA_ERR_INVALID, "vsa_profile_heads: bad sizes");
-    if (dtype != VSA_BF16) return fail(VSA_ERR_UNSUPPORTED, "vsa_profile_heads: only bf16 inputs");
-    if (D != 128) return fail(VSA_ERR_UNSUPPORTED, "vsa_profile_heads: D must be 128");
-    if (bs < 1 || bs > 1024) return fail(VSA_ERR_INVALID, "vsa_profile_heads: bs must be in [1, 1024]");
-    if (P < 1 || P > kProfMaxP) return fail(VSA_ERR_INVALID, "vsa_profile_heads: P must be in [1, %d]", kProfMaxP);
-    if (R < 1) return fail(VSA_ERR_INVALID, "vsa_profile_heads: R must be >= 1");
-    if (!(scale > 0.f) || !__builtin_isfinite(scale)) return fail(VSA_ERR_INVALID, "vsa_profile_heads: scale must be positive and finite");
+        return fail(VSA_ERR_INVALID, "%s: null pointer", fn);
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v)) return fail(VSA_ERR_INVALID, "%s: q, k, v must be 16-byte aligned", fn);
+    if (B <= 0 || H <= 0 || g.T <= 0 || g.Hh <= 0 || g.W <= 0) return fail(VSA_ERR_INVALID, "%s: bad sizes", fn);
+    if (dtype != VSA_BF16) return fail(VSA_ERR_UNSUPPORTED, "%s: only bf16 inputs", fn);
+    if (D != 128) return fail(VSA_ERR_UNSUPPORTED, "%s: D must be 128", fn);
+    if (bs < 1 || bs > 1024) return fail(VSA_ERR_INVALID, "%s: bs must be in [1, 1024]", fn);
+    if (P < 1 || P > kProfMaxP) return fail(VSA_ERR_INVALID, "%s: P must be in [1, %d]", fn, kProfMaxP);
+    if (R < 1) return fail(VSA_ERR_INVALID, "%s: R must be >= 1", fn);
+    if (!(scale > 0.f) || !__builtin_isfinite(scale)) return fail(VSA_ERR_INVALID, "%s: scale must be positive and finite", fn);
     for (int p = 0; p < P; ++p)
         if (cand_layout[p] != 0 && cand_layout[p] != 1)
-            return fail(VSA_ERR_INVALID, "vsa_profile_heads: cand_layout[%d] must be 0 or 1", p);
+            return fail(VSA_ERR_INVALID, "%s: cand_layout[%d] must be 0 or 1", fn, p);
     const int64_t N = (int64_t)g.T * g.Hh * g.W;
-    if (N >= (1ll << 31) || R > N) return fail(VSA_ERR_INVALID, "vsa_profile_heads: bad N or R");
-    if ((int64_t)B * H > 65535 || R > 65535) return fail(VSA_ERR_INVALID, "vsa_profile_heads: B*H or R too large");
-    const ProfPlan pl = prof_plan(B, H, N, D, R, P);
+    if (N >= (1ll << 31) || R > N) return fail(VSA_ERR_INVALID, "%s: bad N or R", fn);
+    if ((int64_t)B * H > 65535 || R > 65535) return fail(VSA_ERR_INVALID, "%s: B*H or R too large", fn);
+    pl = prof_plan(B, H, N, D, R, P);
     if ((int64_t)P * R * pl.words * 4 >= (1ll << 31))
-        return fail(VSA_ERR_INVALID, "vsa_profile_heads: candidate bit table exceeds 2 GiB (R or N too large)");
-    if (!workspace || ws_bytes < pl.total)
-        return fail(VSA_ERR_WORKSPACE, "vsa_profile_heads: workspace of %zu bytes needed (got %zu)", pl.total, ws_bytes);
-    hipStream_t s = as_stream(stream);
-    uint8_t* ws = static_cast<uint8_t*>(workspace);
+        return fail(VSA_ERR_INVALID, "%s: candidate bit table exceeds 2 GiB (R or N too large)", fn);
+    return VSA_OK;
+}
 
+// The launches of one profile, with the scratch at ws (pl.total bytes). Every
+// scratch byte a kernel reads was written earlier in the same sequence, so the
+// scratch needs no clearing.
+int profile_launch(const void* q, const void* k, const void* v, int B, int H, vsa_grid g, int D, int bs,
+                   const int32_t* rows, int R, const uint8_t* cand_masks, const int32_t* cand_layout, int P,
+                   float scale, float* err, int32_t* choice, const ProfPlan& pl, uint8_t* ws, hipStream_t s) {
+    const int64_t N = (int64_t)g.T * g.Hh * g.W;
     BitsArgs ba;
     ba.rows = rows; ba.masks = cand_masks; ba.bits = reinterpret_cast<uint32_t*>(ws + pl.off_bits);
     ba.R = R; ba.N = (int32_t)N; ba.nb = (int32_t)((N + bs - 1) / bs); ba.bs = bs; ba.words = pl.words; ba.P = P;
@@ -591,4 +600,77 @@ extern "C" int vsa_profile_heads(const void* q, const void* k, const void* v, in
     if (st) return st;
     hipLaunchKernelGGL(prof_finish_kernel, dim3(B * H), dim3(256), 0, s, ma.errp, R, P, err, choice);
     return launch_status("vsa_profile_heads (finish)");
+}
+
+}  // namespace
+
+extern "C" int vsa_profile_heads(const void* q, const void* k, const void* v, int B, int H, vsa_grid g, int D,
+                                 int dtype, int bs, const int32_t* rows, int R, const uint8_t* cand_masks,
+                                 const int32_t* cand_layout, int P, float scale, float* err, int32_t* choice,
+                                 void* workspace, size_t ws_bytes, void* stream) {
+    const char* fn = "vsa_profile_heads";
+    ProfPlan pl;
+    const int st = profile_check(fn, q, k, v, B, H, g, D, dtype, bs, rows, R, cand_masks, cand_layout, P, scale, err,
+                                 choice, pl);
+    if (st != VSA_OK) return st;
+    if (!workspace || ws_bytes < pl.total)
+        return fail(VSA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed (got %zu)", fn, pl.total, ws_bytes);
+    return profile_launch(q, k, v, B, H, g, D, bs, rows, R, cand_masks, cand_layout, P, scale, err, choice, pl,
+                          static_cast<uint8_t*>(workspace), as_stream(stream));
+}
+
+// ---------------------------------------------------------------------------
+// Allocation-free variant: the profile's scratch (candidate bit table, split-K
+// partial records, per-row errors) lives in this static device array instead of
+// a caller workspace. The device address of the array is looked up once per
+// device (its host-side name is only a stand-in) and kept; every call on a
+// device shares that device's copy.
+constexpr size_t kProfScratchBytes = (size_t)96 << 20;
+static __device__ __align__(256) uint8_t scratch[kProfScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices] = {};
+
+// Device address of this device's scratch (looked up on the first call).
+int scratch_address(const char* fn, uint8_t** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(VSA_ERR_LAUNCH, "%s: hipGetDevice failed: %s", fn, hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices) return fail(VSA_ERR_UNSUPPORTED, "%s: device %d beyond %d", fn, dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_dev[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(VSA_ERR_LAUNCH, "%s: hipGetSymbolAddress of the static scratch failed: %s", fn,
+                        hipGetErrorString(e));
+        g_scratch_dev[dev] = p;
+    }
+    *out = static_cast<uint8_t*>(g_scratch_dev[dev]);
+    return VSA_OK;
+}
+}  // namespace
+
+extern "C" size_t vsa_profile_scratch_capacity(void) { return kProfScratchBytes; }
+
+extern "C" int vsa_profile_heads_noalloc(const void* q, const void* k, const void* v, int B, int H, vsa_grid g,
+                                         int D, int dtype, int bs, const int32_t* rows, int R,
+                                         const uint8_t* cand_masks, const int32_t* cand_layout, int P, float scale,
+                                         float* err, int32_t* choice, void* stream) {
+    const char* fn = "vsa_profile_heads_noalloc";
+    ProfPlan pl;
+    int st = profile_check(fn, q, k, v, B, H, g, D, dtype, bs, rows, R, cand_masks, cand_layout, P, scale, err,
+                           choice, pl);
+    if (st != VSA_OK) return st;
+    if (pl.total > kProfScratchBytes)
+        return fail(VSA_ERR_WORKSPACE,
+                    "%s: this problem needs %zu bytes of scratch, more than the %zu bytes of static scratch; "
+                    "use vsa_profile_heads with a workspace", fn, pl.total, kProfScratchBytes);
+    uint8_t* ws = nullptr;
+    st = scratch_address(fn, &ws);
+    if (st != VSA_OK) return st;
+    return profile_launch(q, k, v, B, H, g, D, bs, rows, R, cand_masks, cand_layout, P, scale, err, choice, pl, ws,
+                          as_stream(stream));
 }

@@ -192,6 +192,26 @@ int vsa_profile_heads(const void* q, const void* k, const void* v, int B, int H,
                       float* err, int32_t* choice, void* workspace, size_t ws_bytes,
                       void* stream);
 
+/* vsa_profile_heads without a workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc). Same arguments, results and errors as
+ * vsa_profile_heads minus (workspace, ws_bytes); the scratch the profile needs
+ * (vsa_profile_workspace_bytes of the same sizes) comes from a static device
+ * array of vsa_profile_scratch_capacity() bytes (96 MiB: enough for the
+ * Wan 480p and HunyuanVideo 720p shapes at 1 % rows and two candidates) that
+ * every GPU the library runs on holds until the process ends. A problem that
+ * needs more returns VSA_ERR_WORKSPACE before any HIP call. The library
+ * allocates nothing: the first call on a device looks up that device's copy of
+ * the array (hipGetSymbolAddress), later calls reuse it. Every call on one GPU
+ * shares that GPU's scratch, so calls that overlap on one GPU (other streams,
+ * other threads) race; calls in order on one stream do not. The scratch keeps
+ * the last call's contents; no result depends on them. */
+size_t vsa_profile_scratch_capacity(void);
+int vsa_profile_heads_noalloc(const void* q, const void* k, const void* v, int B, int H, vsa_grid g,
+                              int D, int dtype, int bs, const int32_t* rows, int R,
+                              const uint8_t* cand_masks, const int32_t* cand_layout, int P, float scale,
+                              float* err, int32_t* choice, void* stream);
+
 /* Mask -> compacted block list (ascending indices of the 1s of each row).
  *   mask           device uint8: [B, H, nqb, nkb] when head_mask_idx is NULL;
  *                  otherwise [P, nqb, nkb] and head h of every batch uses
