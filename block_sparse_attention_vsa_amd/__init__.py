@@ -22,6 +22,7 @@ VSA_BF16, VSA_F32 = 0, 1
 VSA_PERM_FRAME_MAJOR, VSA_PERM_CUBE4 = 0, 1
 VSA_PATTERN_SPATIAL, VSA_PATTERN_TEMPORAL = 0, 1
 VSA_FP8_ROWS, VSA_FP8_VT = 0, 1
+VSA_SKIPARSE_TOKEN, VSA_SKIPARSE_GROUP = 0, 1
 
 
 class vsa_grid(ctypes.Structure):
@@ -49,6 +50,10 @@ _SIGNATURES = {
     "vsa_pattern_mask": (_I, [vsa_grid, _I, _I, _I, _P, _P]),
     "vsa_cube_block_len": (_I, [vsa_grid, _P, _P]),
     "vsa_permute": (_I, [_P, _P, _I, _I, vsa_grid, _I, _I, _I, _I, _P, _P]),
+    "vsa_skiparse_dims": (_I, [vsa_grid, _I, _I, _I, _P, _P]),
+    "vsa_skiparse_block_len": (_I, [vsa_grid, _I, _I, _I, _P, _P]),
+    "vsa_skiparse_mask": (_I, [vsa_grid, _I, _I, _I, _P, _P]),
+    "vsa_skiparse_permute": (_I, [_P, _P, _I, _I, vsa_grid, _I, _I, _I, _I, _I, _I, _P]),
     "vsa_block_scores": (_I, [_P, _P, _I, _I, _I, _I, _I, _I, _P, _F, _P, _P, _P, _P]),
     "vsa_select_topk": (_I, [_P, _I, _I, _I, _I, _P, _I, _F, _P, _P, _P]),
     "vsa_profile_workspace_bytes": (_SZ, [_I, _I, vsa_grid, _I, _I, _I]),
@@ -303,6 +308,54 @@ def vsa_permute(src, grid, kind: int, inverse: bool = False, head_sel=None, out=
     _on_device(src, out=out)
     _check(lib().vsa_permute(_ptr(src), _ptr(out), B, H, _grid(grid), D, _dtype_code(src), kind, int(bool(inverse)),
                              hs, _stream(src.device)), "vsa_permute")
+    return out
+
+
+def vsa_skiparse_dims(grid, mode: int, k: int, bs: int):
+    """(n_slots, n_blocks) of the padded Skiparse-2D layout."""
+    ns, nb = ctypes.c_int32(), ctypes.c_int32()
+    _check(lib().vsa_skiparse_dims(_grid(grid), mode, k, bs, ctypes.byref(ns), ctypes.byref(nb)), "vsa_skiparse_dims")
+    return ns.value, nb.value
+
+
+def vsa_skiparse_block_len(grid, mode: int, k: int, bs: int, device="cuda", out=None):
+    torch = _torch()
+    _, nb = vsa_skiparse_dims(grid, mode, k, bs)
+    if out is None:
+        out = torch.empty((nb,), dtype=torch.int32, device=device)
+    _expect(out, "out", (nb,), torch.int32)
+    _on_device(out)
+    _check(lib().vsa_skiparse_block_len(_grid(grid), mode, k, bs, _ptr(out), _stream(out.device)),
+           "vsa_skiparse_block_len")
+    return out
+
+
+def vsa_skiparse_mask(grid, mode: int, k: int, bs: int, device="cuda", out=None):
+    torch = _torch()
+    _, nb = vsa_skiparse_dims(grid, mode, k, bs)
+    if out is None:
+        out = torch.empty((nb, nb), dtype=torch.uint8, device=device)
+    _expect(out, "out", (nb, nb), torch.uint8)
+    _on_device(out)
+    _check(lib().vsa_skiparse_mask(_grid(grid), mode, k, bs, _ptr(out), _stream(out.device)), "vsa_skiparse_mask")
+    return out
+
+
+def vsa_skiparse_permute(src, grid, mode: int, k: int, bs: int, inverse: bool = False, out=None):
+    torch = _torch()
+    _expect(src, "src", ndim=4)
+    B, H, rows_in, D = src.shape
+    N = int(np.prod(grid))
+    n_slots, _ = vsa_skiparse_dims(grid, mode, k, bs)
+    want_in, rows_out = (n_slots, N) if inverse else (N, n_slots)
+    if rows_in != want_in:
+        raise ValueError(f"src must hold {want_in} rows per head for this layout, got {rows_in}")
+    if out is None:
+        out = torch.empty((B, H, rows_out, D), dtype=src.dtype, device=src.device)
+    _expect(out, "out", (B, H, rows_out, D), src.dtype)
+    _on_device(src, out=out)
+    _check(lib().vsa_skiparse_permute(_ptr(src), _ptr(out), B, H, _grid(grid), D, _dtype_code(src), mode, k, bs,
+                                      int(bool(inverse)), _stream(src.device)), "vsa_skiparse_permute")
     return out
 
 

@@ -21,7 +21,9 @@
 //    the accumulator holds the keys (bits 2 and 3 of the key index swapped).
 //  * The grid is remapped so that consecutive query blocks of a head run on the
 //    same XCD (workgroups are dealt round-robin over the 8 XCDs), which keeps
-//    the overlapping key windows of neighbouring query blocks in that XCD's L2.
+//    the overlapping key windows of neighbouring query blocks in that XCD's L2;
+//    when heads read different chosen patterns, every XCD takes an equal share
+//    of each pattern's heads.
 #include <math.h>
 
 #include "mfma_tile.h"
@@ -214,6 +216,25 @@ __global__ __launch_bounds__(BS * 2) void attn_fwd_bf16_kernel(AttnArgs a) {
 //  * Softmax keeps a running offset m per query that only moves when a tile's
 //    max exceeds it by more than 8 (log2 units), so O is rarely rescaled; p stays
 //    below 2^8 and the final O / l is unchanged.
+// Work item of workgroup `bid` when every head reads its chosen candidate: the
+// heads are grouped by choice (an invalid choice is a group of its own) and
+// each XCD takes an equal contiguous share of every group (group_remap), so a
+// mix of heavy and light patterns loads the XCDs evenly. -1: use xcd_remap
+// (more than 64 heads, or a problem too small to share).
+__device__ int chosen_item(const AttnArgs& a, int bid) {
+    const int BH = a.num_items / a.nb;
+    if (BH > 64) return -1;
+    uint64_t gm[kGroups] = {0, 0, 0, 0, 0};
+    for (int h = 0; h < BH; ++h) {
+        const int c = ld_const(a.head_choice, h);
+        const int g = (unsigned)c < (unsigned)a.n_cand ? c : kGroups - 1;
+#pragma unroll
+        for (int gg = 0; gg < kGroups; ++gg)
+            if (g == gg) gm[gg] |= 1ull << h;
+    }
+    return group_remap(bid, a.num_items, a.nb, gm);
+}
+
 __device__ __forceinline__ int block_valid_c(const int32_t* blk_len, int b, int BS, int N) {
     int exist = min(BS, N - b * BS);
     return blk_len ? min(ld_const(blk_len, b), exist) : exist;
@@ -240,7 +261,8 @@ __global__ __launch_bounds__(BS * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: LDS copy targets stay scalar
     const int l32 = lane & 31, half = lane >> 5;
     const int nqb = a.nb, nkb = a.nb;
-    const int item = xcd_remap(blockIdx.x, a.num_items);
+    int item = a.head_choice ? chosen_item(a, blockIdx.x) : -1;
+    if (item < 0) item = xcd_remap(blockIdx.x, a.num_items);
     const int bh = item / nqb, qb = item - bh * nqb;
     const int64_t head_off = (int64_t)bh * a.N * D;
     const int valid_q = block_valid_c(a.blk_len, qb, BS, a.N);

@@ -2,6 +2,8 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <vector>
+
 #include "vsa_internal.h"
 
 namespace vsa {
@@ -89,6 +91,57 @@ int vsa_selftest_host(void) {
         for (uint32_t n = 0; n < 300000; n += 7)
             if (f.div(n) != n / d) return vsa::fail(VSA_ERR_INVALID, "FastDiv(%u) wrong at %u", d, n);
     }
+    const int pst = vsa::permute_selftest_host();
+    if (pst != VSA_OK) return pst;
+    // group_remap: a bijection on [0, G) (or -1 everywhere) for head counts,
+    // block counts and group patterns around the video shapes; with one group it
+    // is xcd_remap, and every XCD gets an equal share (+-1 item) of each group
+    const int nbs[] = {1, 2, 3, 5, 7, 8, 9, 31, 256, 929, 1536};
+    const int heads[] = {1, 2, 3, 7, 8, 12, 24, 64};
+    std::vector<int> seen;
+    for (int nb : nbs)
+        for (int BH : heads)
+            for (int pat = 0; pat < 6; ++pat) {
+                uint64_t gm[vsa::kGroups] = {0, 0, 0, 0, 0};
+                for (int h = 0; h < BH; ++h) {
+                    int g = 0;
+                    if (pat == 1) g = h & 1;
+                    if (pat == 2) g = (h % 3 == 1) ? 4 : 0;
+                    if (pat == 3) g = (h * 7 + 3) % 5;
+                    if (pat == 4) g = h < BH / 2 ? 2 : 1;
+                    if (pat == 5) g = (h == BH - 1) ? 3 : 1;
+                    gm[g] |= 1ull << h;
+                }
+                const int G = BH * nb;
+                seen.assign(G, 0);
+                const int first = vsa::group_remap(0, G, nb, gm);
+                int ngroups = 0;
+                for (int g = 0; g < vsa::kGroups; ++g) ngroups += gm[g] != 0;
+                long share[8][vsa::kGroups] = {};
+                for (int bid = 0; bid < G; ++bid) {
+                    const int it = vsa::group_remap(bid, G, nb, gm);
+                    if ((it < 0) != (first < 0))
+                        return vsa::fail(VSA_ERR_INVALID, "group_remap: mixed fallback nb=%d heads=%d", nb, BH);
+                    if (it < 0) continue;
+                    if (it >= G || seen[it]++)
+                        return vsa::fail(VSA_ERR_INVALID, "group_remap: not a bijection nb=%d heads=%d pat=%d", nb,
+                                         BH, pat);
+                    if (ngroups == 1 && it != vsa::xcd_remap(bid, G))
+                        return vsa::fail(VSA_ERR_INVALID, "group_remap: one group differs from xcd_remap");
+                    for (int g = 0; g < vsa::kGroups; ++g)
+                        if ((gm[g] >> (it / nb)) & 1) share[bid & 7][g]++;
+                }
+                if (first < 0) {
+                    if (nb >= 32) return vsa::fail(VSA_ERR_INVALID, "group_remap: fallback at nb=%d", nb);
+                    continue;
+                }
+                for (int g = 0; g < vsa::kGroups; ++g) {
+                    const long Gg = (long)__builtin_popcountll(gm[g]) * nb;
+                    for (int x = 0; x < 8; ++x)
+                        if (share[x][g] < Gg / 8 - vsa::kGroups || share[x][g] > Gg / 8 + vsa::kGroups)
+                            return vsa::fail(VSA_ERR_INVALID, "group_remap: unequal share nb=%d heads=%d", nb, BH);
+                }
+            }
     return VSA_OK;
 }
 

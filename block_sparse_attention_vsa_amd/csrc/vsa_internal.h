@@ -14,6 +14,7 @@ namespace vsa {
 // status, so that entry points can `return fail(VSA_ERR_INVALID, "...")`.
 int fail(int status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
 int launch_status(const char* what);   // VSA_OK or VSA_ERR_LAUNCH after a launch
+int permute_selftest_host();           // host check of the layout maps (permute.hip)
 
 inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
@@ -58,10 +59,62 @@ struct FastDiv {
 // dispatch over the 8 XCDs). Returns the item it should process so that each
 // XCD owns a contiguous range of items, [x q + min(x, r), ...) with q = G / 8,
 // r = G % 8: neighbouring items then share that XCD's L2. A bijection on [0, G).
-__device__ __forceinline__ int xcd_remap(int bid, int G) {
+__host__ __device__ __forceinline__ int xcd_remap(int bid, int G) {
     const int x = bid & 7, j = bid >> 3;
     const int q = G >> 3, r = G & 7;
-    return x * q + min(x, r) + j;
+    return x * q + (x < r ? x : r) + j;
+}
+
+// Work items of heads that run different patterns, dealt evenly over the XCDs.
+// Items are (head, block) pairs, item = head * nb + block, G = heads * nb. Heads
+// are grouped (gm[g] has bit h set for each head h of group g, heads < 64,
+// groups < kGroups); every XCD takes a contiguous 1/8 of every group's items,
+// the last non-empty group what the XCD's workgroup count leaves, so each XCD
+// does an equal share of every group's work whatever the groups cost. Inside a
+// share, items stay in head and block order (neighbouring blocks of a head
+// share that XCD's L2). With one group this is xcd_remap. Returns -1 when a
+// share would be negative (a tiny problem); callers then use xcd_remap.
+constexpr int kGroups = 5;
+__host__ __device__ __forceinline__ int group_remap(int bid, int G, int nb, const uint64_t (&gm)[kGroups]) {
+    const int x = bid & 7, j = bid >> 3;
+    const int q = G >> 3, r = G & 7;
+    int last = -1;
+    for (int g = 0; g < kGroups; ++g)
+        if (gm[g]) last = g;
+    if (last < 0) return -1;
+    // items of group g (not the last) that XCD xx takes, and where they start
+    auto size_of = [&](int g, int xx) -> int {
+        const int64_t Gg = (int64_t)__builtin_popcountll(gm[g]) * nb;
+        return (int)((((int64_t)xx + 1) * Gg >> 3) - ((int64_t)xx * Gg >> 3));
+    };
+    auto size_last = [&](int xx) -> int {
+        int s = q + (xx < r ? 1 : 0);
+        for (int g = 0; g < last; ++g)
+            if (gm[g]) s -= size_of(g, xx);
+        return s;
+    };
+    int lo_last = 0;
+    for (int xx = 0; xx < 8; ++xx) {
+        const int s = size_last(xx);
+        if (s < 0) return -1;
+        if (xx < x) lo_last += s;
+    }
+    int off = 0;
+    for (int g = 0; g <= last; ++g) {
+        if (!gm[g]) continue;
+        const int64_t Gg = (int64_t)__builtin_popcountll(gm[g]) * nb;
+        const int lo = g == last ? lo_last : (int)((int64_t)x * Gg >> 3);
+        const int sz = g == last ? size_last(x) : size_of(g, x);
+        if (j < off + sz) {
+            const int t = lo + (j - off);
+            const int k = t / nb, blk = t - k * nb;
+            uint64_t m = gm[g];
+            for (int i = 0; i < k; ++i) m &= m - 1;      // k-th head of the group
+            return __builtin_ctzll(m) * nb + blk;
+        }
+        off += sz;
+    }
+    return -1;
 }
 
 }  // namespace vsa

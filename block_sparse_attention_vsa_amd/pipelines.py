@@ -14,6 +14,9 @@ their outputs; every step runs in a HIP kernel.
 * semantic_layer: Sparse VideoGen2 page, Abstract: k-means of Q and K per head,
   cluster-major storage, size-weighted top-p over cluster pairs, attention over
   the kept clusters without padding, and O moved back to natural order.
+* skiparse_layer: OSP-Next page, "Method": a fixed token-wise or group-wise
+  spatial pattern, stored subset by subset so it is a block-diagonal mask of
+  dense tiles.
 """
 from __future__ import annotations
 
@@ -23,7 +26,8 @@ from . import (VSA_PATTERN_SPATIAL, VSA_PATTERN_TEMPORAL, VSA_PERM_CUBE4, VSA_PE
                vsa_block_scores, vsa_block_sparse_attn_fwd, vsa_block_sparse_attn_fwd_chosen,
                vsa_cube_block_len, vsa_cube_dims, vsa_mask_to_list,
                vsa_pattern_mask, vsa_permute, vsa_profile_heads, vsa_select_topk, vsa_kmeans,
-               vsa_cluster_order, vsa_gather_rows, vsa_cluster_scores, vsa_varlen_sparse_attn_fwd)
+               vsa_cluster_order, vsa_gather_rows, vsa_cluster_scores, vsa_varlen_sparse_attn_fwd,
+               vsa_skiparse_block_len, vsa_skiparse_mask, vsa_skiparse_permute)
 
 
 def svg_masks(grid, bs, w_spatial, w_temporal, device="cuda"):
@@ -123,4 +127,23 @@ def semantic_layer(q, k, v, Cq, Ck, iters, top_p, k_max=None, scale=None, stats=
     if stats is not None:
         stats.update(q_centroids=cq, k_centroids=ck, q_labels=lq, k_labels=lk, q_counts=nq, k_counts=nk,
                      q_perm=pq, k_perm=pk, q_off=oq, k_off=ok, scores=S, kv_idx=idx, kv_cnt=cnt)
+    return o
+
+
+def skiparse_layer(q, k, v, grid, mode, k_factor, bs=128, scale=None, stats=None):
+    """Returns o in natural order: Q, K, V moved subset by subset, block-sparse
+    attention under the block-diagonal mask with the blocks' valid lengths, O
+    moved back."""
+    qs = vsa_skiparse_permute(q, grid, mode, k_factor, bs)
+    ks = vsa_skiparse_permute(k, grid, mode, k_factor, bs)
+    vs = vsa_skiparse_permute(v, grid, mode, k_factor, bs)
+    blk = vsa_skiparse_block_len(grid, mode, k_factor, bs, device=q.device)
+    m = vsa_skiparse_mask(grid, mode, k_factor, bs, device=q.device)
+    B, H = q.shape[:2]
+    mask = m.expand(B, H, -1, -1).contiguous()
+    idx, cnt = vsa_mask_to_list(mask)
+    os_ = vsa_block_sparse_attn_fwd(qs, ks, vs, bs, kv_idx=idx, kv_cnt=cnt, blk_len=blk, scale=scale)
+    o = vsa_skiparse_permute(os_, grid, mode, k_factor, bs, inverse=True)
+    if stats is not None:
+        stats.update(mask=m, blk_len=blk, kv_idx=idx, kv_cnt=cnt, permuted=(qs, ks, vs), o_permuted=os_)
     return o

@@ -66,6 +66,12 @@ enum vsa_pattern {
     VSA_PATTERN_TEMPORAL = 1  /* |s_q - s_k| <= w, s = y*W + x, in frame-major order */
 };
 
+/* Skiparse-2D patterns (vsa_skiparse_*). */
+enum vsa_skiparse_mode {
+    VSA_SKIPARSE_TOKEN = 0,   /* subset (y mod k, x mod k)                          */
+    VSA_SKIPARSE_GROUP = 1    /* subset ((y div k) mod k, (x div k) mod k): k x k patches */
+};
+
 /* FP8 layouts (vsa_fp8_quantize). */
 enum vsa_fp8_kind {
     VSA_FP8_ROWS = 0,         /* [B, H, N, D] codes, one scale per (b, h, 64 rows)          */
@@ -135,6 +141,35 @@ int vsa_cube_block_len(vsa_grid g, int32_t* blk_len, void* stream);
  *   Bit-exact: pure data movement. */
 int vsa_permute(const void* src, void* dst, int B, int H, vsa_grid g, int D, int dtype,
                 int kind, int inverse, const uint8_t* head_sel, void* stream);
+
+/* ---- Skiparse-2D fixed spatial patterns -----------------------------------
+ * OSP-Next page, "Method": the sparse attention uses fixed token-wise and
+ * group-wise patterns along the spatial axes, kept FlashAttention-compatible.
+ * Reading (the page gives no more): factor k in [1, 8]; a token (t, y, x)
+ * belongs to subset a*k + b with (a, b) = (y mod k, x mod k) (token-wise) or
+ * ((y div k) mod k, (x div k) mod k) (group-wise: contiguous k x k patches, k
+ * patches apart); a query attends to every key of its subset, in every frame.
+ * Stored subset by subset (subsets in id order, each padded to a whole number
+ * of bs-slot blocks, its tokens in its first slots in natural order) the pattern
+ * is a block-diagonal block mask, so the flow is
+ *   vsa_skiparse_permute(Q, K, V) -> vsa_block_sparse_attn_fwd(bs, mask from
+ *   vsa_skiparse_mask, blk_len from vsa_skiparse_block_len) ->
+ *   vsa_skiparse_permute(O, inverse = 1).
+ * mode is VSA_SKIPARSE_TOKEN or VSA_SKIPARSE_GROUP; bs in [1, 1024]. */
+
+/* Padded layout size (host only): n_slots = n_blocks * bs. */
+int vsa_skiparse_dims(vsa_grid g, int mode, int k, int bs, int32_t* n_slots, int32_t* n_blocks);
+/* Valid slots of each block: out, device int32 [n_blocks]. */
+int vsa_skiparse_block_len(vsa_grid g, int mode, int k, int bs, int32_t* blk_len, void* stream);
+/* Block-diagonal mask: out, device uint8 [n_blocks, n_blocks], 1 where both
+ * blocks belong to the same subset. */
+int vsa_skiparse_mask(vsa_grid g, int mode, int k, int bs, uint8_t* mask, void* stream);
+/* Move Q, K, V to the padded layout (inverse = 0: [B, H, N, D] -> [B, H, n_slots, D],
+ * pad slots zero-filled) or O back (inverse = 1: [B, H, n_slots, D] -> [B, H, N, D]).
+ * dtype VSA_BF16 or VSA_F32; D in {64, 128}; src and dst must not overlap.
+ * Bit-exact: pure data movement. */
+int vsa_skiparse_permute(const void* src, void* dst, int B, int H, vsa_grid g, int D, int dtype, int mode,
+                         int k, int bs, int inverse, void* stream);
 
 /* Block mean-pooling and pooled scores.
  * USV page, Figure 2 caption: long-range key cubes are chosen by top-k cube

@@ -198,3 +198,21 @@ def test_fp8_calls_check_their_buffers():
     shape_error(V.vsa_block_sparse_attn_fwd_fp8, q8, q8, z((1, 2, 4, 128, 64), U8), qs, qs, vs, 128, mask=m)
     shape_error(V.vsa_block_sparse_attn_fwd_fp8, q8, q8, vt8, z((1, 2, 4), F32), qs, vs, 128, mask=m)
     shape_error(V.vsa_block_sparse_attn_fwd_fp8, q8, q8, vt8, qs, qs, vs, 128, mask=z((1, 2, 3, 2), U8))
+
+
+def test_skiparse_calls_check_their_buffers():
+    grid = (2, 9, 7)                       # N = 126
+    n_slots, nb = V.vsa_skiparse_dims(grid, V.VSA_SKIPARSE_GROUP, 3, 64)
+    x = z((1, 2, 126, 128))
+    reaches_device_check(V.vsa_skiparse_permute, x, grid, V.VSA_SKIPARSE_GROUP, 3, 64)
+    shape_error(V.vsa_skiparse_permute, z((1, 2, 125, 128)), grid, V.VSA_SKIPARSE_GROUP, 3, 64)
+    shape_error(V.vsa_skiparse_permute, x, grid, V.VSA_SKIPARSE_GROUP, 3, 64, out=z((1, 2, n_slots - 1, 128)))
+    shape_error(V.vsa_skiparse_permute, x, grid, V.VSA_SKIPARSE_GROUP, 3, 64, inverse=True)
+    reaches_device_check(V.vsa_skiparse_permute, z((1, 2, n_slots, 128)), grid, V.VSA_SKIPARSE_GROUP, 3, 64,
+                         inverse=True)
+    shape_error(V.vsa_skiparse_block_len, grid, V.VSA_SKIPARSE_GROUP, 3, 64, out=z((nb + 1,), I32))
+    shape_error(V.vsa_skiparse_mask, grid, V.VSA_SKIPARSE_GROUP, 3, 64, out=z((nb, nb + 1), U8))
+    with pytest.raises(V.VsaError):
+        V.vsa_skiparse_dims(grid, 2, 3, 64)
+    with pytest.raises(V.VsaError):
+        V.vsa_skiparse_dims(grid, V.VSA_SKIPARSE_TOKEN, 9, 64)
