@@ -11,9 +11,13 @@ in HBM before the timed region. Prints one JSON line.
 `value` is the step's effective throughput: kept attention flops (4 D per valid
 query-key pair of every kept block) divided by the step time. `roofline`
 describes the attention kernel alone, timed with HIP events on its own stream.
-The cube top-p/top-k layer and the long-horizon layer are timed once per run as
-extra sub-step figures. `cpu_baseline` is the fp64 CPU oracle on a sample of
-query blocks of the same workload, on this host's cores.
+`extra_layers` times the other layers of the pages at their shapes (the 6/6
+spatial/temporal split, the backward, FP8, Skiparse-2D, HunyuanVideo, the cube
+top-p/top-k layer, the long horizon, the semantic layer), each step as device
+work queued behind a lead spin so that no host latency sits inside an event
+pair, with dense attention at the same shape for the speedups. `cpu_baseline`
+is the fp64 CPU oracle on a sample of query blocks of the same workload, on this
+host's cores.
 """
 from __future__ import annotations
 
@@ -247,6 +251,27 @@ class Timer:
         e.record()
         return e
 
+    def lead(self, ms=3.0):
+        """A device spin of about `ms` milliseconds (at most; the counter runs at
+        the shader clock) queued before timed work: the host queues the timed
+        calls while the GPU is still busy, so the event pairs that follow bracket
+        device work only, never the host's launch latency."""
+        self.torch.cuda._sleep(int(ms * 2.4e6))
+
+    def per_call_ms(self, fn, reps, warm=1):
+        """Device time of fn per call: `reps` calls queued back to back behind a
+        lead spin long enough for the host to queue all of them."""
+        for _ in range(warm):
+            fn()
+        self.torch.cuda.synchronize()
+        self.lead(max(3.0, 0.3 * reps))
+        e0 = self.ev()
+        for _ in range(reps):
+            fn()
+        e1 = self.ev()
+        self.torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
     def add(self, key, e0, e1):
         self.acc.setdefault(key, []).append((e0, e1))
 
@@ -325,46 +350,15 @@ def main():
     comp = {key: round(T.mean_ms(key), 4) for key in T.acc}
 
     # dense baselines at the same [B, H, N, D]
-    ones = torch.ones((B, H, w.nb, w.nb), dtype=torch.uint8, device=dev)
-    for _ in range(2):
-        V.vsa_block_sparse_attn_fwd(q, k, v, bs, mask=ones)
-    torch.cuda.synchronize()
-    e0 = T.ev()
-    for _ in range(3):
-        V.vsa_block_sparse_attn_fwd(q, k, v, bs, mask=ones)
-    e1 = T.ev()
-    torch.cuda.synchronize()
-    dense_ours = e0.elapsed_time(e1) / 3
-    dense_sdpa = None
-    try:
-        import torch.nn.functional as F
-        for _ in range(2):
-            F.scaled_dot_product_attention(q, k, v)
-        torch.cuda.synchronize()
-        e0 = T.ev()
-        for _ in range(3):
-            F.scaled_dot_product_attention(q, k, v)
-        e1 = T.ev()
-        torch.cuda.synchronize()
-        dense_sdpa = e0.elapsed_time(e1) / 3
-    except Exception as ex:   # report, do not hide
-        print(f"bench.py: torch SDPA baseline failed: {ex}", file=sys.stderr)
-    dense_ms = min(x for x in (dense_ours, dense_sdpa) if x is not None)
+    dense = dense_baselines(torch, V, T, q, k, v, bs)
+    dense_ours, dense_sdpa, dense_ms = dense["ours_all_blocks"], dense["torch_sdpa"], dense["best"]
 
     n_moved = sum(sel)
     # the standalone permutation kernel (a3 / a8 as separate calls), every head
     # moved: read + write of one [B, H, N, D] tensor per call
     all_heads = [1] * H
     pdst = torch.empty_like(q)
-    for _ in range(2):
-        V.vsa_permute(q, grid, V.VSA_PERM_FRAME_MAJOR, False, all_heads, out=pdst)
-    torch.cuda.synchronize()
-    e0 = T.ev()
-    for _ in range(10):
-        V.vsa_permute(q, grid, V.VSA_PERM_FRAME_MAJOR, False, all_heads, out=pdst)
-    e1 = T.ev()
-    torch.cuda.synchronize()
-    perm_ms = e0.elapsed_time(e1) / 10
+    perm_ms = T.per_call_ms(lambda: V.vsa_permute(q, grid, V.VSA_PERM_FRAME_MAJOR, False, all_heads, out=pdst), 10)
     perm_gbs = 2 * q.numel() * q.element_size() / (perm_ms * 1e-3) / 1e9
     del pdst
 
@@ -375,7 +369,7 @@ def main():
 
     extra = {}
     if not args.no_extra:
-        extra = extra_layers(torch, V, PL, T)
+        extra = extra_layers(torch, V, PL, T, dense, attn_tflops)
 
     digest = source_digest("attn_fwd.hip", "mfma_tile.h", "vsa_internal.h")
     # the chosen-candidate launch carries the frame-major loop whenever a
@@ -430,11 +424,34 @@ def main():
     print(json.dumps(out), flush=True)
 
 
+def dense_baselines(torch, V, T, q, k, v, bs, reps=3):
+    """Dense attention at the shape of q: this library with every tile kept (the
+    all-ones block mask) and torch's scaled_dot_product_attention; `best` is the
+    faster, the denominator of a speedup. A backend torch lacks at this size is
+    reported as None."""
+    B, H, N, D = q.shape
+    nb = -(-N // bs)
+    ones = torch.ones((B, H, nb, nb), dtype=torch.uint8, device=q.device)
+    ours = T.per_call_ms(lambda: V.vsa_block_sparse_attn_fwd(q, k, v, bs, mask=ones), reps)
+    del ones
+    sdpa = None
+    try:
+        import torch.nn.functional as F
+        sdpa = T.per_call_ms(lambda: F.scaled_dot_product_attention(q, k, v), reps)
+    except Exception as ex:   # report, do not hide
+        print(f"bench.py: torch SDPA baseline failed at N={N}: {str(ex)[:200]}", file=sys.stderr)
+    torch.cuda.empty_cache()
+    best = min(x for x in (ours, sdpa) if x is not None)
+    return {"ours_all_blocks": round(ours, 3), "torch_sdpa": None if sdpa is None else round(sdpa, 3),
+            "best": best, "dense_flops": 4.0 * B * H * N * N * D}
+
+
 def launch_stats(torch, T, fn, flops, runs=50, warm=5, flush_bytes=1 << 30):
     """One kernel launch timed alone: `runs` launches after `warm`, each bracketed
-    by HIP events on the current stream; warm (back to back) and cold (a 1 GiB
-    buffer written before each launch, which evicts L2 and the 256 MB MALL).
-    Median, p10, p90 in ms and TFLOP/s at the median."""
+    by HIP events on the current stream behind a lead spin (so the bracket holds
+    no host latency); warm (inputs left in the caches by the previous launch) and
+    cold (a 1 GiB buffer written before each launch, which evicts L2 and the
+    256 MB MALL). Median, p10, p90 in ms and TFLOP/s at the median."""
     dev = torch.device("cuda:0")
     buf = torch.empty((flush_bytes,), dtype=torch.uint8, device=dev)
     out = {}
@@ -444,6 +461,7 @@ def launch_stats(torch, T, fn, flops, runs=50, warm=5, flush_bytes=1 << 30):
         torch.cuda.synchronize()
         ts = []
         for i in range(runs):
+            T.lead(1.0)                      # the launch below is queued before the GPU gets to it
             if mode == "cold":
                 buf.fill_(i & 255)
             e0 = T.ev()
@@ -510,8 +528,9 @@ def environment(torch):
 
 
 def time_backward(torch, V, T, q, k, v, bs, fwd_flops, reps=4, **blocks):
-    """Forward (with LSE) once, then the backward under the same block set, timed
-    over reps - 1 calls after one untimed call; dO is seeded unit normal."""
+    """Forward (with LSE) once, then the backward under the same block set: device
+    time per call over reps - 1 calls queued back to back after one untimed
+    call; dO is seeded unit normal."""
     g = torch.Generator(device=q.device).manual_seed(7)
     do = torch.randn(q.shape, generator=g, device=q.device, dtype=torch.float32).to(q.dtype)
     o, lse = V.vsa_block_sparse_attn_fwd(q, k, v, bs, return_lse=True, **blocks)
@@ -519,15 +538,9 @@ def time_backward(torch, V, T, q, k, v, bs, fwd_flops, reps=4, **blocks):
     ws = torch.empty((V.vsa_attn_bwd_workspace_bytes(B, H, N, bs, "kv_idx" in blocks),), dtype=torch.uint8,
                      device=q.device)
     grads = [torch.empty_like(q) for _ in range(3)]
-    ms = []
-    for rep in range(reps):
-        e0 = T.ev()
-        V.vsa_block_sparse_attn_bwd(q, k, v, o, lse, do, bs, dq=grads[0], dk=grads[1], dv=grads[2], workspace=ws,
-                                    **blocks)
-        e1 = T.ev()
-        torch.cuda.synchronize()
-        if rep:
-            ms.append(e0.elapsed_time(e1))
+    t = T.per_call_ms(lambda: V.vsa_block_sparse_attn_bwd(q, k, v, o, lse, do, bs, dq=grads[0], dk=grads[1],
+                                                            dv=grads[2], workspace=ws, **blocks), reps - 1)
+    ms = [t]
     t = float(np.mean(ms))
     fl = 2.5 * fwd_flops          # 10 D per kept pair (S, dP, dV, dQ, dK) against the forward's 4 D
     del do, o, lse, ws, grads
@@ -535,49 +548,77 @@ def time_backward(torch, V, T, q, k, v, bs, fwd_flops, reps=4, **blocks):
             "pct_mfma_peak": round(100 * fl / (t * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2)}
 
 
-def extra_layers(torch, V, PL, T):
-    """Cube top-p/top-k layer (Wan shape) and long-horizon layer, each timed over a
-    few runs with per-call events: the pooling/score and selection steps live here."""
+def queued(torch, T, steps, reps):
+    """Device time of each labelled call of a sequence: the sequence is queued
+    `reps` times back to back behind a lead spin, with an event between calls,
+    and timed on repetitions 1 .. reps-1 (repetition 0 is a warm-up). `steps` is
+    a list of (label, fn); returns ({label: mean ms}, the last outputs)."""
+    torch.cuda.synchronize()
+    T.lead(max(3.0, 0.4 * reps * len(steps)))
+    marks, outs = [], {}
+    for rep in range(reps):
+        e = [T.ev()]
+        for label, fn in steps:
+            outs[label] = fn()
+            e.append(T.ev())
+        if rep:
+            marks.append(e)
+    torch.cuda.synchronize()
+    ms = {}
+    for e in marks:
+        for n, (label, _) in enumerate(steps):
+            ms.setdefault(label, []).append(e[n].elapsed_time(e[n + 1]))
+    return {label: round(float(np.mean(v_)), 4) for label, v_ in ms.items()}, outs
+
+
+def speedups(dense, attn_ms, layer_ms):
+    return {"dense_ms": {"ours_all_blocks": dense["ours_all_blocks"], "torch_sdpa": dense["torch_sdpa"]},
+            "speedup_vs_dense_kernel": round(dense["best"] / attn_ms, 2),
+            "speedup_vs_dense_pipeline": round(dense["best"] / layer_ms, 2)}
+
+
+def extra_layers(torch, V, PL, T, wan_dense, wan_attn_tflops):
+    """The other layers of the pages at their shapes, each step timed as device
+    work (queued behind a lead spin, so no host latency is inside a bracket),
+    with the dense baselines at the same shape for the speedups."""
     res = {}
     dev = torch.device("cuda:0")
 
     # Wan 480p with a 6/6 head split (even heads spatial w=1, odd heads temporal
-    # w=0 in frame-major order): the fused kernel against the separate sequence
-    # permute x3 -> attention -> inverse permute.
+    # w=0 in frame-major order): the step's kernel with the choice read on the
+    # device, the same kernel with host lists, and the separate sequence
+    # permute x3 -> attention -> inverse permute
     w = WAN480
     q, k, v = (torch.from_numpy(x).to(torch.bfloat16).to(dev) for x in make_qkv(w))
     sel = [h % 2 for h in range(w.H)]
+    ch = torch.tensor([sel], dtype=torch.int32, device=dev)
     cand = PL.svg_masks(w.grid, w.bs, w.extra["w_spatial"], w.extra["w_temporal"], dev)
     idx, cnt = V.vsa_mask_to_list(cand, head_mask_idx=sel, B=1)
     FMK = V.VSA_PERM_FRAME_MAJOR
-    times = {}
-    for rep in range(4):
-        e = [T.ev()]
-        o_f = V.vsa_block_sparse_attn_fwd_permuted(q, k, v, w.grid, w.bs, head_fm=sel, kv_idx=idx, kv_cnt=cnt)
-        e.append(T.ev())
-        qm = V.vsa_permute(q, w.grid, FMK, False, sel)
-        km = V.vsa_permute(k, w.grid, FMK, False, sel)
-        vm = V.vsa_permute(v, w.grid, FMK, False, sel)
-        e.append(T.ev())
-        om = V.vsa_block_sparse_attn_fwd(qm, km, vm, w.bs, kv_idx=idx, kv_cnt=cnt)
-        e.append(T.ev())
-        o_s = V.vsa_permute(om, w.grid, FMK, True, sel)
-        e.append(T.ev())
-        torch.cuda.synchronize()
-        if rep:
-            for key, i in (("fused_attention", 0), ("separate_permute_qkv", 1), ("separate_attention", 2),
-                           ("separate_permute_o", 3)):
-                times.setdefault(key, []).append(e[i].elapsed_time(e[i + 1]))
-    if not torch.equal(o_f, o_s):
-        print("bench.py: fused and separate frame-major paths disagree", file=sys.stderr)
+    qm, km, vm, om, o_s = (torch.empty_like(q) for _ in range(5))
+    o_c = V.vsa_block_sparse_attn_fwd_chosen(q, k, v, w.grid, w.bs, cand, [0, 1], ch)
+    o_f = V.vsa_block_sparse_attn_fwd_permuted(q, k, v, w.grid, w.bs, head_fm=sel, kv_idx=idx, kv_cnt=cnt)
+    ms = {"chosen_attention": T.per_call_ms(
+              lambda: V.vsa_block_sparse_attn_fwd_chosen(q, k, v, w.grid, w.bs, cand, [0, 1], ch, out=o_c), 5),
+          "fused_attention": T.per_call_ms(
+              lambda: V.vsa_block_sparse_attn_fwd_permuted(q, k, v, w.grid, w.bs, head_fm=sel, kv_idx=idx,
+                                                           kv_cnt=cnt, out=o_f), 5),
+          "separate_permute_qkv": T.per_call_ms(
+              lambda: [V.vsa_permute(x, w.grid, FMK, False, sel, out=y) for x, y in ((q, qm), (k, km), (v, vm))], 5),
+          "separate_attention": T.per_call_ms(
+              lambda: V.vsa_block_sparse_attn_fwd(qm, km, vm, w.bs, kv_idx=idx, kv_cnt=cnt, out=om), 5),
+          "separate_permute_o": T.per_call_ms(lambda: V.vsa_permute(om, w.grid, FMK, True, sel, out=o_s), 5)}
+    ms = {k_: round(v_, 4) for k_, v_ in ms.items()}
     fl = kept_flops_from_lists(idx, cnt, w.N, w.bs, 128)
-    ms = {k_: round(float(np.mean(v_)), 4) for k_, v_ in times.items()}
-    res["svg_6_6_split_wan480"] = {"ms": ms, "kept_flops": fl,
-                                   "fused_attn_tflops": round(fl / (ms["fused_attention"] * 1e-3) / 1e12, 2),
-                                   "separate_total_ms": round(ms["separate_permute_qkv"] + ms["separate_attention"]
-                                                              + ms["separate_permute_o"], 4),
-                                   "bit_identical": bool(torch.equal(o_f, o_s))}
-    del qm, km, vm, om, o_f, o_s, cand
+    split_tflops = fl / (ms["chosen_attention"] * 1e-3) / 1e12
+    res["svg_6_6_split_wan480"] = {
+        "ms": ms, "kept_flops": fl, "chosen_attn_tflops": round(split_tflops, 2),
+        "fused_attn_tflops": round(fl / (ms["fused_attention"] * 1e-3) / 1e12, 2),
+        "rate_vs_all_spatial_step_kernel": round(split_tflops / wan_attn_tflops, 3),
+        "separate_total_ms": round(ms["separate_permute_qkv"] + ms["separate_attention"] + ms["separate_permute_o"], 4),
+        "bit_identical": bool(torch.equal(o_c, o_f) and torch.equal(o_f, o_s)),
+        **speedups(wan_dense, ms["chosen_attention"], ms["chosen_attention"])}
+    del qm, km, vm, om, o_f, o_s, o_c, cand, ch
     torch.cuda.empty_cache()
 
     # backward (dQ, dK, dV) at the same shape with the spatial w=1 block mask on
@@ -593,24 +634,16 @@ def extra_layers(torch, V, PL, T):
     # FP8 (e4m3) attention under the same mask: quantisation of Q, K, V, then the
     # fp8 kernel, against the bf16 kernel on the same inputs
     fl_sp = kept_flops_from_lists(bi, bc, w.N, w.bs, 128)
-    times, reps = {}, []
-    for rep in range(4):                     # queued ahead, one sync at the end
-        e = [T.ev()]
-        q8, qs = V.vsa_fp8_quantize(q, V.VSA_FP8_ROWS)
-        k8, ks = V.vsa_fp8_quantize(k, V.VSA_FP8_ROWS)
-        vt8, vs8 = V.vsa_fp8_quantize(v, V.VSA_FP8_VT)
-        e.append(T.ev())
-        o8 = V.vsa_block_sparse_attn_fwd_fp8(q8, k8, vt8, qs, ks, vs8, w.bs, mask=mask)
-        e.append(T.ev())
-        ob = V.vsa_block_sparse_attn_fwd(q, k, v, w.bs, mask=mask)
-        e.append(T.ev())
-        if rep:
-            reps.append(e)
-    torch.cuda.synchronize()
-    for e in reps:
-        for key, i in (("quantise_qkv", 0), ("fp8_attention", 1), ("bf16_attention", 2)):
-            times.setdefault(key, []).append(e[i].elapsed_time(e[i + 1]))
-    ms = {k_: round(float(np.mean(v_)), 4) for k_, v_ in times.items()}
+    q8, qsc = V.vsa_fp8_quantize(q, V.VSA_FP8_ROWS)
+    k8, ksc = V.vsa_fp8_quantize(k, V.VSA_FP8_ROWS)
+    vt8, vsc = V.vsa_fp8_quantize(v, V.VSA_FP8_VT)
+    o8, ob = torch.empty_like(q), torch.empty_like(q)
+    ms, _ = queued(torch, T, [
+        ("quantise_qkv", lambda: (V.vsa_fp8_quantize(q, V.VSA_FP8_ROWS, out=q8, scales=qsc),
+                                  V.vsa_fp8_quantize(k, V.VSA_FP8_ROWS, out=k8, scales=ksc),
+                                  V.vsa_fp8_quantize(v, V.VSA_FP8_VT, out=vt8, scales=vsc))),
+        ("fp8_attention", lambda: V.vsa_block_sparse_attn_fwd_fp8(q8, k8, vt8, qsc, ksc, vsc, w.bs, mask=mask, out=o8)),
+        ("bf16_attention", lambda: V.vsa_block_sparse_attn_fwd(q, k, v, w.bs, mask=mask, out=ob))], 4)
     rel = float(((o8.float() - ob.float()).abs().mean() / ob.float().abs().mean()).item())
     res["fp8_spatial_wan480"] = {"ms": ms, "kept_flops": fl_sp,
                                  "fp8_attn_tflops": round(fl_sp / (ms["fp8_attention"] * 1e-3) / 1e12, 2),
@@ -619,8 +652,38 @@ def extra_layers(torch, V, PL, T):
                                                             / PEAK_FP8_TFLOPS, 2),
                                  "speedup_vs_bf16": round(ms["bf16_attention"] / ms["fp8_attention"], 3),
                                  "mean_rel_diff_vs_bf16": round(rel, 4)}
-    del q8, k8, vt8, o8, ob
-    del q, k, v, m, mask, bi, bc
+    del q8, k8, vt8, o8, ob, m, mask, bi, bc
+
+    # Skiparse-2D (OSP-Next page, "Method"), k = 2, both patterns, at the Wan shape
+    for mode_name, mode in (("token", V.VSA_SKIPARSE_TOKEN), ("group", V.VSA_SKIPARSE_GROUP)):
+        kf, sbs = 2, 128
+        ns, nbk = V.vsa_skiparse_dims(w.grid, mode, kf, sbs)
+        qs_, ks_, vs_, os_ = (torch.empty((1, w.H, ns, w.D), dtype=q.dtype, device=dev) for _ in range(4))
+        o = torch.empty_like(q)
+        blk = V.vsa_skiparse_block_len(w.grid, mode, kf, sbs)
+        sm = V.vsa_skiparse_mask(w.grid, mode, kf, sbs)
+        smask = sm.expand(1, w.H, -1, -1).contiguous()
+        si, sc = V.vsa_mask_to_list(smask)
+        ms, _ = queued(torch, T, [
+            ("permute_qkv", lambda: [V.vsa_skiparse_permute(x, w.grid, mode, kf, sbs, out=y)
+                                     for x, y in ((q, qs_), (k, ks_), (v, vs_))]),
+            ("mask_and_lists", lambda: (V.vsa_skiparse_block_len(w.grid, mode, kf, sbs, out=blk),
+                                        V.vsa_skiparse_mask(w.grid, mode, kf, sbs, out=sm),
+                                        V.vsa_mask_to_list(smask, out=(si, sc)))),
+            ("attention", lambda: V.vsa_block_sparse_attn_fwd(qs_, ks_, vs_, sbs, kv_idx=si, kv_cnt=sc, blk_len=blk,
+                                                              out=os_)),
+            ("permute_o", lambda: V.vsa_skiparse_permute(os_, w.grid, mode, kf, sbs, inverse=True, out=o))], 4)
+        fl = kept_flops_from_lists(si, sc, ns, sbs, 128, blk)
+        layer = sum(ms.values())
+        res[f"skiparse_{mode_name}_k2_wan480"] = {
+            "ms": ms, "layer_ms": round(layer, 4), "kept_flops": fl,
+            "kept_pair_density": round(fl / (4.0 * w.D * w.H * w.N * w.N), 4),
+            "attn_tflops": round(fl / (ms["attention"] * 1e-3) / 1e12, 2),
+            "pct_mfma_peak": round(100 * fl / (ms["attention"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+            "permute_GBps": round(3 * (q.numel() + qs_.numel()) * 2 / (ms["permute_qkv"] * 1e-3) / 1e9, 1),
+            **speedups(wan_dense, ms["attention"], layer)}
+        del qs_, ks_, vs_, os_, o, blk, sm, smask, si, sc
+    del q, k, v
     torch.cuda.empty_cache()
 
     # HunyuanVideo 720p layer (24 heads, 118,800 tokens): planted 12/12 split, even
@@ -630,116 +693,112 @@ def extra_layers(torch, V, PL, T):
     w = HUNYUAN720
     q, k, v = (torch.from_numpy(x).to(torch.bfloat16).to(dev) for x in make_qkv(w))
     sel = [h % 2 for h in range(w.H)]
+    ch = torch.tensor([sel], dtype=torch.int32, device=dev)
     cand = PL.svg_masks(w.grid, w.bs, w.extra["w_spatial"], w.extra["w_temporal"], dev)
     idx, cnt = V.vsa_mask_to_list(cand, head_mask_idx=sel, B=1)
     fl = kept_flops_from_lists(idx, cnt, w.N, w.bs, 128)
-    ts = []
-    for rep in range(4):
-        e0 = T.ev()
-        o = V.vsa_block_sparse_attn_fwd_permuted(q, k, v, w.grid, w.bs, head_fm=sel, kv_idx=idx, kv_cnt=cnt)
-        e1 = T.ev()
-        torch.cuda.synchronize()
-        if rep:
-            ts.append(e0.elapsed_time(e1))
-    t_att = float(np.mean(ts))
+    o = torch.empty_like(q)
+    ms, _ = queued(torch, T, [
+        ("masks", lambda: PL.svg_masks(w.grid, w.bs, w.extra["w_spatial"], w.extra["w_temporal"], dev)),
+        ("chosen_attention", lambda: V.vsa_block_sparse_attn_fwd_chosen(q, k, v, w.grid, w.bs, cand, [0, 1], ch,
+                                                                         out=o))], 3)
+    t_att = ms["chosen_attention"]
     pdst = torch.empty_like(q)
-    for _ in range(2):
-        V.vsa_permute(q, w.grid, V.VSA_PERM_FRAME_MAJOR, False, [1] * w.H, out=pdst)
-    torch.cuda.synchronize()
-    e0 = T.ev()
-    for _ in range(10):
-        V.vsa_permute(q, w.grid, V.VSA_PERM_FRAME_MAJOR, False, [1] * w.H, out=pdst)
-    e1 = T.ev()
-    torch.cuda.synchronize()
-    p_ms = e0.elapsed_time(e1) / 10
+    p_ms = T.per_call_ms(lambda: V.vsa_permute(q, w.grid, V.VSA_PERM_FRAME_MAJOR, False, [1] * w.H, out=pdst), 10)
     p_gbs = 2 * q.numel() * q.element_size() / (p_ms * 1e-3) / 1e9
-    res["svg_hunyuan720"] = {"attention_ms": round(t_att, 3), "kept_flops": fl,
+    del pdst
+    dense = dense_baselines(torch, V, T, q, k, v, w.bs, reps=2)
+    res["svg_hunyuan720"] = {"ms": ms, "attention_ms": round(t_att, 3), "kept_flops": fl,
                              "attn_tflops": round(fl / (t_att * 1e-3) / 1e12, 2),
                              "pct_mfma_peak": round(100 * fl / (t_att * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
                              "permute_all_heads": {"ms": round(p_ms, 4), "GBps": round(p_gbs, 1),
                                                    "frac_of_hbm_peak": round(p_gbs / PEAK_HBM_GBS, 3),
                                                    "bytes": 2 * q.numel() * q.element_size()},
-                             "what": "vsa_block_sparse_attn_fwd_permuted, [1,24,118800,128] bf16, bs 128"}
-    del q, k, v, o, pdst, cand, idx, cnt
+                             **speedups(dense, t_att, sum(ms.values())),
+                             "what": "vsa_block_sparse_attn_fwd_chosen, [1,24,118800,128] bf16, bs 128, planted split"}
+    del q, k, v, o, cand, idx, cnt, ch
     torch.cuda.empty_cache()
 
     w = WAN480_CUBE
     q, k, v = (torch.from_numpy(x).to(torch.bfloat16).to(dev) for x in make_qkv(w))
     n_cubes, k_max = PL.cube_budget(w.grid, w.extra["k_frac"])
     blk = V.vsa_cube_block_len(w.grid)
-    times, reps = {}, []
-    # no host sync inside the loop: the host queues ahead, so each event pair
-    # brackets GPU work only, not the host's launch latency
-    for rep in range(4):
-        e = [T.ev()]
-        qc = V.vsa_permute(q, w.grid, V.VSA_PERM_CUBE4)
-        kc = V.vsa_permute(k, w.grid, V.VSA_PERM_CUBE4)
-        vc = V.vsa_permute(v, w.grid, V.VSA_PERM_CUBE4)
-        e.append(T.ev())
-        S, _, _ = V.vsa_block_scores(qc, kc, 64, blk_len=blk)
-        e.append(T.ev())
-        idx, cnt = V.vsa_select_topk(S, k_max, w.extra["top_p"])
-        e.append(T.ev())
-        oc = V.vsa_block_sparse_attn_fwd(qc, kc, vc, 64, kv_idx=idx, kv_cnt=cnt, blk_len=blk)
-        e.append(T.ev())
-        o = V.vsa_permute(oc, w.grid, V.VSA_PERM_CUBE4, inverse=True)
-        e.append(T.ev())
-        if rep:
-            reps.append(e)
-    torch.cuda.synchronize()
-    for e in reps:
-        for key, i in (("a3_cube_permute_qkv", 0), ("a4_block_scores", 1), ("a5_select_topk", 2),
-                       ("a7_attention", 3), ("a8_cube_permute_o", 4)):
-            times.setdefault(key, []).append(e[i].elapsed_time(e[i + 1]))
+    st = {}
+
+    def cube_permute():
+        st["qc"], st["kc"], st["vc"] = (V.vsa_permute(x, w.grid, V.VSA_PERM_CUBE4) for x in (q, k, v))
+
+    def cube_scores():
+        st["S"] = V.vsa_block_scores(st["qc"], st["kc"], 64, blk_len=blk)[0]
+
+    def cube_select():
+        st["idx"], st["cnt"] = V.vsa_select_topk(st["S"], k_max, w.extra["top_p"])
+
+    def cube_attn():
+        st["oc"] = V.vsa_block_sparse_attn_fwd(st["qc"], st["kc"], st["vc"], 64, kv_idx=st["idx"], kv_cnt=st["cnt"],
+                                               blk_len=blk)
+
+    def cube_back():
+        st["o"] = V.vsa_permute(st["oc"], w.grid, V.VSA_PERM_CUBE4, inverse=True)
+
+    ms, _ = queued(torch, T, [("a3_cube_permute_qkv", cube_permute), ("a4_block_scores", cube_scores),
+                              ("a5_select_topk", cube_select), ("a7_attention", cube_attn),
+                              ("a8_cube_permute_o", cube_back)], 4)
+    qc, kc, vc, S, idx, cnt, oc = (st[x] for x in ("qc", "kc", "vc", "S", "idx", "cnt", "oc"))
     fl = kept_flops_from_lists(idx, cnt, oc.shape[2], 64, 128, blk)
-    t_att = float(np.mean(times["a7_attention"]))
+    t_att = ms["a7_attention"]
     nat_b = q.numel() * q.element_size()                         # one natural-order tensor
     cube_b = qc.numel() * qc.element_size()                      # one cube-major tensor, pad slots included
     gbs = {"a3_cube_permute_qkv": 3 * (nat_b + cube_b),          # read every token, write every slot
            "a4_block_scores": 2 * nat_b + S.numel() * 4,         # the valid rows of Q and K read, S written
            "a8_cube_permute_o": cube_b + nat_b}
-    hbm = {key: {"GBps": round(b / (np.mean(times[key]) * 1e-3) / 1e9, 1),
-                 "frac_of_hbm_peak": round(b / (np.mean(times[key]) * 1e-3) / 1e9 / PEAK_HBM_GBS, 3)}
+    hbm = {key: {"GBps": round(b / (ms[key] * 1e-3) / 1e9, 1),
+                 "frac_of_hbm_peak": round(b / (ms[key] * 1e-3) / 1e9 / PEAK_HBM_GBS, 3)}
            for key, b in gbs.items()}
-    res["cube_topp_wan480"] = {"ms": {k_: round(float(np.mean(v_)), 4) for k_, v_ in times.items()},
-                               "hbm": hbm,
+    res["cube_topp_wan480"] = {"ms": ms, "layer_ms": round(sum(ms.values()), 4), "hbm": hbm,
                                "k_max": k_max, "mean_kept": round(float(cnt.float().mean().item()), 2),
-                               "attn_tflops": round(fl / (t_att * 1e-3) / 1e12, 2),
+                               "kept_flops": fl, "attn_tflops": round(fl / (t_att * 1e-3) / 1e12, 2),
+                               "pct_mfma_peak": round(100 * fl / (t_att * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+                               **speedups(wan_dense, t_att, sum(ms.values())),
                                "backward": time_backward(torch, V, T, qc, kc, vc, 64, fl, kv_idx=idx, kv_cnt=cnt,
                                                          blk_len=blk)}
-    del q, k, v, qc, kc, vc, oc, o, S
+    del q, k, v, qc, kc, vc, oc, S, st
     torch.cuda.empty_cache()
 
     w = LONG126
     q, k, v = (torch.from_numpy(x).to(torch.bfloat16).to(dev) for x in make_qkv(w))
     k_total = int(round(w.extra["density"] * w.nb))
-    times, reps = {}, []
-    for rep in range(3):
-        e = [T.ev()]
-        forced = V.vsa_pattern_mask(w.grid, w.bs, V.VSA_PATTERN_SPATIAL, w.extra["w_local"])
-        e.append(T.ev())
-        S, _, _ = V.vsa_block_scores(q, k, w.bs)
-        e.append(T.ev())
-        idx, cnt = V.vsa_select_topk(S, k_total, 1.0, forced=forced)
-        e.append(T.ev())
-        o = V.vsa_block_sparse_attn_fwd(q, k, v, w.bs, kv_idx=idx, kv_cnt=cnt)
-        e.append(T.ev())
-        if rep:
-            reps.append(e)
-    torch.cuda.synchronize()
-    for e in reps:
-        for key, i in (("a1_local_mask", 0), ("a4_block_scores", 1), ("a5_select_topk", 2), ("a7_attention", 3)):
-            times.setdefault(key, []).append(e[i].elapsed_time(e[i + 1]))
+    st = {}
+
+    def long_mask():
+        st["forced"] = V.vsa_pattern_mask(w.grid, w.bs, V.VSA_PATTERN_SPATIAL, w.extra["w_local"])
+
+    def long_scores():
+        st["S"] = V.vsa_block_scores(q, k, w.bs)[0]
+
+    def long_select():
+        st["idx"], st["cnt"] = V.vsa_select_topk(st["S"], k_total, 1.0, forced=st["forced"])
+
+    def long_attn():
+        st["o"] = V.vsa_block_sparse_attn_fwd(q, k, v, w.bs, kv_idx=st["idx"], kv_cnt=st["cnt"])
+
+    ms, _ = queued(torch, T, [("a1_local_mask", long_mask), ("a4_block_scores", long_scores),
+                              ("a5_select_topk", long_select), ("a7_attention", long_attn)], 3)
+    S, idx, cnt = st["S"], st["idx"], st["cnt"]
     fl = kept_flops_from_lists(idx, cnt, w.N, w.bs, 128)
-    t_att = float(np.mean(times["a7_attention"]))
+    t_att = ms["a7_attention"]
     a4_b = 2 * q.numel() * q.element_size() + S.numel() * 4      # Q and K read once, S written
-    a4_gbs = a4_b / (np.mean(times["a4_block_scores"]) * 1e-3) / 1e9
-    res["long_horizon_126x30x52"] = {"ms": {k_: round(float(np.mean(v_)), 4) for k_, v_ in times.items()},
+    a4_gbs = a4_b / (ms["a4_block_scores"] * 1e-3) / 1e9
+    del st, S
+    dense = dense_baselines(torch, V, T, q, k, v, w.bs, reps=2)
+    res["long_horizon_126x30x52"] = {"ms": ms, "layer_ms": round(sum(ms.values()), 4),
                                      "hbm": {"a4_block_scores": {"GBps": round(a4_gbs, 1),
                                                                  "frac_of_hbm_peak": round(a4_gbs / PEAK_HBM_GBS, 3)}},
-                                     "k_total": k_total, "attn_tflops": round(fl / (t_att * 1e-3) / 1e12, 2),
-                                     "pct_mfma_peak": round(100 * fl / (t_att * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2)}
-    del q, k, v, o, S
+                                     "k_total": k_total, "kept_flops": fl,
+                                     "attn_tflops": round(fl / (t_att * 1e-3) / 1e12, 2),
+                                     "pct_mfma_peak": round(100 * fl / (t_att * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+                                     **speedups(dense, t_att, sum(ms.values()))}
+    del q, k, v
     torch.cuda.empty_cache()
 
     # Sparse VideoGen2-style layer: k-means of Q and K, cluster-major storage,
@@ -747,47 +806,50 @@ def extra_layers(torch, V, PL, T):
     w = WAN480_SEMANTIC
     q, k, v = (torch.from_numpy(x).to(torch.bfloat16).to(dev) for x in make_qkv(w))
     Cq, Ck, iters, top_p = w.extra["Cq"], w.extra["Ck"], w.extra["iters"], w.extra["top_p"]
-    times, reps = {}, []
-    for rep in range(4):                     # queued ahead, one sync at the end
-        e = [T.ev()]
-        cq, lq, nq = V.vsa_kmeans(q, Cq, iters)
-        e.append(T.ev())
-        ck, lk, nk = V.vsa_kmeans(k, Ck, iters)
-        e.append(T.ev())
-        pq, oq = V.vsa_cluster_order(lq, Cq)
-        pk, ok = V.vsa_cluster_order(lk, Ck)
-        e.append(T.ev())
-        qs = V.vsa_gather_rows(q, pq)
-        ks = V.vsa_gather_rows(k, pk)
-        vs = V.vsa_gather_rows(v, pk)
-        e.append(T.ev())
-        S = V.vsa_cluster_scores(cq, ck, nk)
-        idx, cnt = V.vsa_select_topk(S, Ck, top_p)
-        e.append(T.ev())
-        os_ = V.vsa_varlen_sparse_attn_fwd(qs, ks, vs, oq, ok, kv_idx=idx, kv_cnt=cnt)
-        e.append(T.ev())
-        o = V.vsa_gather_rows(os_, pq, inverse=True)
-        e.append(T.ev())
-        if rep:
-            reps.append(e)
-    torch.cuda.synchronize()
-    for e in reps:
-        for key, i in (("kmeans_q", 0), ("kmeans_k", 1), ("cluster_order_qk", 2), ("gather_qkv", 3),
-                       ("scores_select", 4), ("varlen_attention", 5), ("gather_o", 6)):
-            times.setdefault(key, []).append(e[i].elapsed_time(e[i + 1]))
-    nqh, nkh, ih, ch = (x.cpu().numpy().astype(np.int64) for x in (nq, nk, idx, cnt))
+    st = {}
+
+    def km_q():
+        st["cq"], st["lq"], st["nq"] = V.vsa_kmeans(q, Cq, iters)
+
+    def km_k():
+        st["ck"], st["lk"], st["nk"] = V.vsa_kmeans(k, Ck, iters)
+
+    def order():
+        st["pq"], st["oq"] = V.vsa_cluster_order(st["lq"], Cq)
+        st["pk"], st["ok"] = V.vsa_cluster_order(st["lk"], Ck)
+
+    def gather():
+        st["qs"] = V.vsa_gather_rows(q, st["pq"])
+        st["ks"] = V.vsa_gather_rows(k, st["pk"])
+        st["vs"] = V.vsa_gather_rows(v, st["pk"])
+
+    def scores_select():
+        st["S"] = V.vsa_cluster_scores(st["cq"], st["ck"], st["nk"])
+        st["idx"], st["cnt"] = V.vsa_select_topk(st["S"], Ck, top_p)
+
+    def attn():
+        st["os"] = V.vsa_varlen_sparse_attn_fwd(st["qs"], st["ks"], st["vs"], st["oq"], st["ok"], kv_idx=st["idx"],
+                                                kv_cnt=st["cnt"])
+
+    def back():
+        st["o"] = V.vsa_gather_rows(st["os"], st["pq"], inverse=True)
+
+    ms, _ = queued(torch, T, [("kmeans_q", km_q), ("kmeans_k", km_k), ("cluster_order_qk", order),
+                              ("gather_qkv", gather), ("scores_select", scores_select), ("varlen_attention", attn),
+                              ("gather_o", back)], 4)
+    nqh, nkh, ih, chh = (st[x].cpu().numpy().astype(np.int64) for x in ("nq", "nk", "idx", "cnt"))
     kept = 0.0
     for h in range(w.H):
         for a in range(Cq):
-            kept += float(nqh[0, h, a]) * float(nkh[0, h, ih[0, h, a, :ch[0, h, a]]].sum())
+            kept += float(nqh[0, h, a]) * float(nkh[0, h, ih[0, h, a, :chh[0, h, a]]].sum())
     fl = 4.0 * w.D * kept
-    ms = {k_: round(float(np.mean(v_)), 4) for k_, v_ in times.items()}
     t_att = ms["varlen_attention"]
     res["semantic_wan480"] = {"ms": ms, "total_ms": round(sum(ms.values()), 4), "Cq": Cq, "Ck": Ck, "iters": iters,
                               "top_p": top_p, "kept_pair_density": round(kept / (w.H * w.N * w.N), 4),
                               "kept_flops": fl, "attn_tflops": round(fl / (t_att * 1e-3) / 1e12, 2),
-                              "pct_mfma_peak": round(100 * fl / (t_att * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2)}
-    del q, k, v, qs, ks, vs, os_, o, S
+                              "pct_mfma_peak": round(100 * fl / (t_att * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+                              **speedups(wan_dense, t_att, sum(ms.values()))}
+    del q, k, v, st
     torch.cuda.empty_cache()
     return res
 

@@ -57,6 +57,10 @@ struct AttnArgs {
     const int32_t* head_choice;
     int32_t n_cand;
     int32_t cand_fm[4];
+    // D = 128 bf16 kernel: int16 entries of the row's block list held in LDS (nb
+    // for the mask form, max_kv for the list form; 0 = the list form reads its
+    // row from global memory); with blk_len, as many valid lengths follow them
+    int32_t lds_cap;
 };
 
 // Natural row of permuted row r (r < N) for a frame-major head.
@@ -252,8 +256,8 @@ __global__ __launch_bounds__(BS * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
     __shared__ __attribute__((aligned(1024))) uint8_t v0[SUBB];
     __shared__ __attribute__((aligned(1024))) uint8_t k1[SUBB];
     __shared__ __attribute__((aligned(1024))) uint8_t v1[SUBB];
-    // mask form only: the compacted row, sized at launch (0 bytes for the list
-    // form, so 64-row blocks fit 4 workgroups per CU)
+    // the row's kept blocks (compacted from the mask, or copied from the list)
+    // and, with blk_len, their valid lengths: sized at launch
     extern __shared__ __attribute__((aligned(16))) int16_t list_lds[];
     __shared__ int wave_cnt[WAVES];
 
@@ -281,21 +285,47 @@ __global__ __launch_bounds__(BS * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
         fm = (a.fm_bits[h >> 5] >> (h & 31)) & 1u;
     }
 
+    // The row's kept blocks go to LDS once, so the loop reads each entry (and its
+    // valid length) from LDS instead of waiting on a global load per sub-tile.
     int cnt;
     const int32_t* list_g = nullptr;
+    int16_t* len_lds = list_lds + a.lds_cap;
+    const bool in_lds = a.mask != nullptr || a.lds_cap > 0;
     if (a.head_choice && !mask_row) {
         cnt = 0;
     } else if (a.mask) {
         cnt = compact_mask_row<THREADS>(mask_row, nkb, list_lds, wave_cnt);
+        if (a.blk_len) {
+            for (int e = tid; e < cnt; e += THREADS) len_lds[e] = (int16_t)block_valid(a.blk_len, list_lds[e], BS, a.N);
+            lds_barrier();
+        }
     } else {
         cnt = min(ld_const(a.kv_cnt, item), a.max_kv);
         list_g = a.kv_idx + (int64_t)item * a.max_kv;
+        if (a.lds_cap > 0) {
+            for (int e = tid; e < cnt; e += THREADS) {
+                const int kb = list_g[e];
+                const bool okb = (unsigned)kb < (unsigned)nkb;
+                list_lds[e] = okb ? (int16_t)kb : (int16_t)-1;     // a malformed entry is skipped
+                if (a.blk_len) len_lds[e] = okb ? (int16_t)block_valid(a.blk_len, kb, BS, a.N) : (int16_t)0;
+            }
+            lds_barrier();
+        }
     }
     // valid keys of sub-tile i (0 when it holds none, or its block entry is malformed)
     auto sub_valid = [&](int i, int& kb) -> int {
-        kb = a.mask ? (int)list_lds[i / SUB] : ld_const(list_g, i / SUB);
-        if ((unsigned)kb >= (unsigned)nkb) return 0;
-        int v = block_valid_c(a.blk_len, kb, BS, a.N) - (i % SUB) * KT;
+        const int e = i / SUB;
+        int v;
+        if (in_lds) {
+            kb = list_lds[e];
+            if ((unsigned)kb >= (unsigned)nkb) return 0;
+            v = a.blk_len ? (int)len_lds[e] : min(BS, a.N - kb * BS);
+        } else {
+            kb = ld_const(list_g, e);
+            if ((unsigned)kb >= (unsigned)nkb) return 0;
+            v = block_valid_c(a.blk_len, kb, BS, a.N);
+        }
+        v -= (i % SUB) * KT;
         return v < 0 ? 0 : (v > KT ? KT : v);
     };
     const SubTileDma<WAVES, kVSwz4, KT> dma(lane, w);
@@ -587,13 +617,22 @@ void launch_attn(const AttnArgs& a, int D, int dtype, int bs, hipStream_t s) {
         for (int i = 0; i < 32; ++i) gather |= a.fm_bits[i] != 0;
         if (a.head_choice)
             for (int c = 0; c < a.n_cand; ++c) gather |= a.cand_fm[c] != 0;
-        const size_t shm = a.mask ? (((size_t)a.nb * 2 + 15) & ~(size_t)15) : 0;
+        // LDS for the row's list (and valid lengths): the mask form always keeps
+        // it there; the list form when it fits beside the K/V stages without
+        // costing a workgroup per CU (2 per CU at bs 128, 4 at bs 64) and the
+        // block ids fit int16
+        AttnArgs b = a;
+        const size_t per_entry = a.blk_len ? 4 : 2;
+        const size_t budget = bs == 128 ? 16384 : 8192;
+        if (a.mask) b.lds_cap = a.nb;
+        else b.lds_cap = ((size_t)a.max_kv * per_entry <= budget && a.nb <= 32767) ? a.max_kv : 0;
+        const size_t shm = ((size_t)b.lds_cap * per_entry + 15) & ~(size_t)15;
         if (D == 128 && bs == 128) {
-            if (gather) hipLaunchKernelGGL((attn_fwd_bf16_d128_kernel<128, true>), grid, dim3(256), shm, s, a);
-            else hipLaunchKernelGGL((attn_fwd_bf16_d128_kernel<128, false>), grid, dim3(256), shm, s, a);
+            if (gather) hipLaunchKernelGGL((attn_fwd_bf16_d128_kernel<128, true>), grid, dim3(256), shm, s, b);
+            else hipLaunchKernelGGL((attn_fwd_bf16_d128_kernel<128, false>), grid, dim3(256), shm, s, b);
         } else if (D == 128 && bs == 64) {
-            if (gather) hipLaunchKernelGGL((attn_fwd_bf16_d128_kernel<64, true>), grid, dim3(128), shm, s, a);
-            else hipLaunchKernelGGL((attn_fwd_bf16_d128_kernel<64, false>), grid, dim3(128), shm, s, a);
+            if (gather) hipLaunchKernelGGL((attn_fwd_bf16_d128_kernel<64, true>), grid, dim3(128), shm, s, b);
+            else hipLaunchKernelGGL((attn_fwd_bf16_d128_kernel<64, false>), grid, dim3(128), shm, s, b);
         }
         else if (D == 64 && bs == 128) hipLaunchKernelGGL((attn_fwd_bf16_kernel<64, 128>), grid, dim3(256), 0, s, a);
         else hipLaunchKernelGGL((attn_fwd_bf16_kernel<64, 64>), grid, dim3(128), 0, s, a);
