@@ -15,7 +15,9 @@ import os
 import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libvsa.so")
+# VSA_LIBRARY names another build of the same library (the host-sanitized one
+# the CPU tests load); by default the in-tree libvsa.so
+LIB_PATH = os.environ.get("VSA_LIBRARY") or os.path.join(HERE, "libvsa.so")
 
 VSA_OK, VSA_ERR_INVALID, VSA_ERR_UNSUPPORTED, VSA_ERR_LAUNCH, VSA_ERR_WORKSPACE = range(5)
 VSA_BF16, VSA_F32 = 0, 1

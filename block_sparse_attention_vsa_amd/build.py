@@ -37,9 +37,18 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def _compile(src: str, verbose: bool) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+# Host-side AddressSanitizer and UndefinedBehaviorSanitizer (device code is
+# compiled as usual): every -fsanitize= is scoped to the host pass.
+SANITIZE_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                  "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer"]
+SAN_BUILD = os.path.join(BUILD, "sanitize")
+SAN_LIB = os.path.join(SAN_BUILD, "libvsa_sanitized.so")
+
+
+def _compile(src: str, verbose: bool, sanitize: bool = False) -> str:
+    out_dir = SAN_BUILD if sanitize else BUILD
+    obj = os.path.join(out_dir, os.path.splitext(src)[0] + ".o")
+    cmd = [hipcc(), *FLAGS, *(SANITIZE_FLAGS if sanitize else []), "-c", os.path.join(CSRC, src), "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     err = "\n".join(l for l in res.stderr.splitlines()
                     if "packed-fp32-ops" not in l and "is not a recognized feature" not in l)
@@ -50,20 +59,35 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False, jobs: int | None = None) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+def build(verbose: bool = False, jobs: int | None = None, sanitize: bool = False) -> str:
+    """Compile every source and link libvsa.so; with sanitize, a separate
+    _build/sanitize/libvsa_sanitized.so whose host code carries ASan and UBSan
+    (load it with the sanitizer runtime preloaded, see sanitizer_runtime())."""
+    os.makedirs(SAN_BUILD if sanitize else BUILD, exist_ok=True)
     srcs = [s for s in SOURCES if os.path.exists(os.path.join(CSRC, s))]
     jobs = jobs or min(len(srcs), os.cpu_count() or 4, 16)
     with cf.ThreadPoolExecutor(jobs) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
+        objs = list(ex.map(lambda s: _compile(s, verbose, sanitize), srcs))
+    lib = SAN_LIB if sanitize else LIB
+    tmp = lib + ".tmp"
+    extra = ["-fsanitize=address", "-fsanitize=undefined", "-shared-libasan"] if sanitize else []
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *extra, "-o", tmp, *objs]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
-        raise RuntimeError(f"linking libvsa.so failed:\n{' '.join(cmd)}\n{res.stderr}")
-    os.replace(tmp, LIB)
-    return LIB
+        raise RuntimeError(f"linking {os.path.basename(lib)} failed:\n{' '.join(cmd)}\n{res.stderr}")
+    os.replace(tmp, lib)
+    return lib
+
+
+def sanitizer_runtime() -> str:
+    """Path of the compiler's shared ASan runtime (to LD_PRELOAD into an
+    uninstrumented Python that loads the sanitized library)."""
+    res = subprocess.run([hipcc(), "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True, text=True)
+    path = res.stdout.strip()
+    if not os.path.isabs(path) or not os.path.exists(path):
+        raise RuntimeError("the clang ASan runtime was not found")
+    return path
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    print(build(verbose="-v" in sys.argv, sanitize="--sanitize" in sys.argv))

@@ -1,6 +1,7 @@
 // Status codes, per-thread error messages and host-only entry points.
 #include <stdarg.h>
 #include <stdio.h>
+#include <stdlib.h>
 
 #include <vector>
 
@@ -10,11 +11,23 @@ namespace vsa {
 
 static thread_local char g_last_error[512] = "";
 
+// Call log: with VSA_TRACE set to a non-empty value other than "0", every
+// launch the library makes and every rejected call is written to stderr, one
+// line each ("[vsa] <call>: <outcome>"), in the order they happen on the host.
+static bool trace_on() {
+    static const bool on = [] {
+        const char* v = getenv("VSA_TRACE");
+        return v && *v && !(v[0] == '0' && v[1] == 0);
+    }();
+    return on;
+}
+
 int fail(int status, const char* fmt, ...) {
     va_list ap;
     va_start(ap, fmt);
     vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
     va_end(ap);
+    if (trace_on()) fprintf(stderr, "[vsa] rejected (status %d): %s\n", status, g_last_error);
     return status;
 }
 
@@ -22,6 +35,7 @@ int launch_status(const char* what) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return fail(VSA_ERR_LAUNCH, "%s: %s", what, hipGetErrorString(e));
+    if (trace_on()) fprintf(stderr, "[vsa] %s: launched\n", what);
     return VSA_OK;
 }
 

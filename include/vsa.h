@@ -33,6 +33,9 @@
  *             No C++ exception crosses this interface.
  * Determinism Results are bit-reproducible from run to run: no floating-point
  *             atomics; every reduction has a fixed order.
+ * Tracing     With the environment variable VSA_TRACE set (not "0"), every
+ *             kernel launch ("[vsa] <call>: launched") and every rejected call
+ *             ("[vsa] rejected (status s): <message>") is logged to stderr.
  */
 #ifndef VSA_H
 #define VSA_H

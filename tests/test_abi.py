@@ -289,3 +289,19 @@ def test_fp8_validation():
     assert at(bs=64) == V.VSA_ERR_UNSUPPORTED
     assert at(scale=-1.0) == V.VSA_ERR_INVALID
     assert at(blocks=V.vsa_blocks()) == V.VSA_ERR_INVALID
+
+
+def test_trace_log_names_rejected_calls():
+    """VSA_TRACE=1 logs every rejected call (and every launch) to stderr; unset,
+    the library prints nothing."""
+    import subprocess
+    import sys
+    code = ("import ctypes, block_sparse_attention_vsa_amd as V; "
+            "print(V.lib().vsa_pattern_mask(V.vsa_grid(4, 8, 8), 0, 0, 1, ctypes.c_void_p(0x1000), None))")
+    on = subprocess.run([sys.executable, "-c", code], env=dict(os.environ, VSA_TRACE="1"), cwd=ROOT,
+                        capture_output=True, text=True, timeout=120)
+    assert on.stdout.strip() == "1"
+    assert "[vsa] rejected (status 1): vsa_pattern_mask: bs must be in [1, 1024]" in on.stderr
+    off = subprocess.run([sys.executable, "-c", code], env=dict(os.environ, VSA_TRACE="0"), cwd=ROOT,
+                         capture_output=True, text=True, timeout=120)
+    assert off.stdout.strip() == "1" and "[vsa]" not in off.stderr
