@@ -61,6 +61,9 @@ struct AttnArgs {
     // for the mask form, max_kv for the list form; 0 = the list form reads its
     // row from global memory); with blk_len, as many valid lengths follow them
     int32_t lds_cap;
+    // heads grouped by a host-known kind (frame-major or not) for the XCD deal;
+    // all zero = no grouping
+    uint64_t head_groups[kGroups];
 };
 
 // Natural row of permuted row r (r < N) for a frame-major head.
@@ -265,7 +268,9 @@ __global__ __launch_bounds__(BS * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: LDS copy targets stay scalar
     const int l32 = lane & 31, half = lane >> 5;
     const int nqb = a.nb, nkb = a.nb;
-    int item = a.head_choice ? chosen_item(a, blockIdx.x) : -1;
+    int item = a.head_choice ? chosen_item(a, blockIdx.x)
+                             : ((a.head_groups[0] | a.head_groups[1])
+                                    ? group_remap(blockIdx.x, a.num_items, a.nb, a.head_groups) : -1);
     if (item < 0) item = xcd_remap(blockIdx.x, a.num_items);
     const int bh = item / nqb, qb = item - bh * nqb;
     const int64_t head_off = (int64_t)bh * a.N * D;
@@ -677,6 +682,18 @@ extern "C" int vsa_block_sparse_attn_fwd_permuted(const void* q, const void* k, 
     if (head_fm)
         for (int h = 0; h < H; ++h)
             if (head_fm[h]) a.fm_bits[h >> 5] |= 1u << (h & 31);
+    // frame-major and natural heads usually run different patterns: deal each
+    // kind evenly over the XCDs (at most 64 heads in all)
+    if (head_fm && (int64_t)B * H <= 64) {
+        bool any_fm = false, any_nat = false;
+        for (int b = 0; b < B; ++b)
+            for (int h = 0; h < H; ++h) {
+                const int bh = b * H + h;
+                a.head_groups[head_fm[h] ? 1 : 0] |= 1ull << bh;
+                (head_fm[h] ? any_fm : any_nat) = true;
+            }
+        if (!(any_fm && any_nat)) a.head_groups[0] = a.head_groups[1] = 0;   // one kind: the plain deal
+    }
     launch_attn(a, D, dtype, bs, as_stream(stream));
     return launch_status(fn);
 }
