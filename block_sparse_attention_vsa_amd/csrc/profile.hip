@@ -22,9 +22,10 @@
 //     serves every set); its P V products run on every sub-tile, with P zero
 //     where the candidate keeps nothing. Each (slot, row, split) writes a
 //     partial record (m, l, O).
-//  3. merge: one workgroup per (b, h, sampled row) combines the partial records
-//     in split order (exact log-sum-exp rescaling), normalises every slot and
-//     sums each candidate's squared difference to the dense output.
+//  3. merge: one wave per (b, h, sampled row) combines the partial records of
+//     every slot (exact log-sum-exp rescaling, the splits' loads in flight
+//     together), normalises them and sums each candidate's squared difference
+//     to the dense output.
 //  4. finish: per (b, h) the row sums are added in a fixed tree order; choice =
 //     first argmin.
 #include <math.h>
@@ -451,38 +452,52 @@ struct MergeArgs {
     int64_t rec;
 };
 
-// One workgroup of D = 128 threads per (b, h, sampled row); thread d merges
-// channel d of every slot over the splits in order (exact log-sum-exp
-// rescaling).
-__global__ __launch_bounds__(128) void prof_merge_kernel(MergeArgs a) {
-    __shared__ float red[kProfMaxP][128];
-    const int ri = blockIdx.x, bh = blockIdx.y, d = threadIdx.x;
-    float dense = 0.f;
+__device__ __forceinline__ float wave_max_f(float x) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+    return x;
+}
+__device__ __forceinline__ float wave_sum_f(float x) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+    return x;
+}
+
+// One wave per (b, h, sampled row), four per workgroup; lane d merges channels
+// d and d + 64 of every set. Lane s holds split s's (m, l) (at most 32 splits),
+// so the common offset and the weight sum come from one load each; the channel
+// loads of the splits are independent of each other. Splits add in split order.
+__global__ __launch_bounds__(256) void prof_merge_kernel(MergeArgs a) {
+    const int lane = threadIdx.x & 63;
+    const int64_t wv = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (wv >= (int64_t)a.R * a.BH) return;                 // whole waves leave together
+    const int bh = (int)(wv / a.R), ri = (int)(wv % a.R);
+    float dense0 = 0.f, dense1 = 0.f;
     for (int slot = 0; slot <= a.P; ++slot) {
         const float* recs = a.part + (((int64_t)slot * a.BH + bh) * a.R + ri) * a.S * a.rec;
-        float m = -INFINITY;
-        for (int s = 0; s < a.S; ++s) m = fmaxf(m, recs[s * a.rec]);
-        float l = 0.f, ov = 0.f;
-        if (m != -INFINITY) {
-            for (int s = 0; s < a.S; ++s) {
-                const float ms = recs[s * a.rec];
-                if (ms == -INFINITY) continue;
-                const float f = __builtin_amdgcn_exp2f(ms - m);
-                l += recs[s * a.rec + 1] * f;
-                ov += recs[s * a.rec + 4 + d] * f;
-            }
+        const float ms = lane < a.S ? recs[lane * a.rec] : -INFINITY;
+        const float ls = lane < a.S ? recs[lane * a.rec + 1] : 0.f;
+        const float m = wave_max_f(ms);
+        const float f = (ms == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ms - m);
+        const float l = wave_sum_f(ls * f);
+        float o0 = 0.f, o1 = 0.f;
+#pragma unroll 8
+        for (int s = 0; s < a.S; ++s) {
+            const float mss = recs[s * a.rec];           // the same address on every lane
+            const float fs = (mss == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mss - m);
+            o0 += recs[s * a.rec + 4 + lane] * fs;
+            o1 += recs[s * a.rec + 68 + lane] * fs;
         }
-        const float out = l > 0.f ? ov / l : 0.f;
-        if (slot == 0) dense = out;
-        else red[slot - 1][d] = (out - dense) * (out - dense);
+        const float out0 = l > 0.f ? o0 / l : 0.f, out1 = l > 0.f ? o1 / l : 0.f;
+        if (slot == 0) {
+            dense0 = out0;
+            dense1 = out1;
+        } else {
+            const float d0 = out0 - dense0, d1 = out1 - dense1;
+            const float e = wave_sum_f(d0 * d0 + d1 * d1);
+            if (lane == 0) a.errp[((int64_t)bh * a.R + ri) * kProfMaxP + slot - 1] = e;
+        }
     }
-    __syncthreads();
-    for (int s = 64; s > 0; s >>= 1) {
-        if (d < s)
-            for (int p = 0; p < a.P; ++p) red[p][d] += red[p][d + s];
-        __syncthreads();
-    }
-    if (d < a.P) a.errp[((int64_t)bh * a.R + ri) * kProfMaxP + d] = red[d][0];
 }
 
 // One workgroup per (b, h): per-row errors summed in a fixed order.
@@ -595,7 +610,7 @@ int profile_launch(const void* q, const void* k, const void* v, int B, int H, vs
     MergeArgs ma;
     ma.part = pa.part; ma.errp = reinterpret_cast<float*>(ws + pl.off_errp);
     ma.R = R; ma.S = pl.S; ma.BH = B * H; ma.P = P; ma.rec = pl.rec;
-    hipLaunchKernelGGL(prof_merge_kernel, dim3(R, B * H), dim3(128), 0, s, ma);
+    hipLaunchKernelGGL(prof_merge_kernel, dim3((unsigned)(((int64_t)R * B * H + 3) / 4)), dim3(256), 0, s, ma);
     st = launch_status("vsa_profile_heads (merge)");
     if (st) return st;
     hipLaunchKernelGGL(prof_finish_kernel, dim3(B * H), dim3(256), 0, s, ma.errp, R, P, err, choice);

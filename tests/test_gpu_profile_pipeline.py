@@ -81,6 +81,27 @@ def test_profile_candidate_counts_and_identical_candidates(P):
         assert np.array_equal(ge[..., 1], ge[..., 3])      # identical candidates, identical errors
 
 
+@pytest.mark.parametrize("bs,shuffle", [(48, True), (64, True), (40, False)])
+def test_profile_ragged_blocks_and_unsorted_rows(bs, shuffle):
+    """Blocks that are not a whole number of 32-key words (bit words built run
+    by run), sampled rows in no particular order (each pass orders them by its
+    layout), and candidates of both layouts, one natural one beyond the dense
+    pass's own."""
+    grid = (5, 9, 11)
+    announce(f"profile ragged bs={bs} shuffle={shuffle}")
+    w, (q, k, v) = small(grid, 3, 0.5, 13, bs)
+    g = np.random.default_rng([13, bs])
+    rows = g.choice(w.N, size=70, replace=False).astype(np.int32)
+    if not shuffle:
+        rows = np.sort(rows)
+    cands = np.stack([OM.pattern_mask(grid, bs, "spatial", 0), OM.pattern_mask(grid, bs, "temporal", 2),
+                      OM.pattern_mask(grid, bs, "spatial", 1)])
+    lay = [0, 1, 0]
+    err, ch = V.vsa_profile_heads(dev(q), dev(k), dev(v), grid, bs, dev_i32(rows), dev_u8(cands), lay)
+    er, cr = OPR.profile_heads(q, k, v, grid, bs, rows, cands, lay)
+    check_profile(host(err), host(ch), er, cr, f"ragged bs={bs}")
+
+
 @pytest.mark.parametrize("amplitude", [0.5, 4.0])
 def test_profile_wan_full_shape(amplitude):
     """The benchmarked launch: Wan 480p, 12 heads, 1 % rows (328), spatial w=1 in
