@@ -562,6 +562,8 @@ int profile_check(const char* fn, const void* q, const void* k, const void* v, i
             return fail(VSA_ERR_INVALID, "%s: cand_layout[%d] must be 0 or 1", fn, p);
     const int64_t N = (int64_t)g.T * g.Hh * g.W;
     if (N >= (1ll << 31) || R > N) return fail(VSA_ERR_INVALID, "%s: bad N or R", fn);
+    // one head of K or V is addressed through a buffer descriptor of N * D * 2 bytes (32-bit size)
+    if (N * D * 2 >= (1ll << 31)) return fail(VSA_ERR_INVALID, "%s: one head exceeds 2 GiB (N too large)", fn);
     if ((int64_t)B * H > 65535 || R > 65535) return fail(VSA_ERR_INVALID, "%s: B*H or R too large", fn);
     pl = prof_plan(B, H, N, D, R, P);
     if ((int64_t)P * R * pl.words * 4 >= (1ll << 31))

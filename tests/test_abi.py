@@ -170,6 +170,12 @@ def test_profile_validation_and_workspace_size():
     bad = (ctypes.c_int32 * 2)(0, 2)
     assert L.vsa_profile_heads(p, p, p, 1, 12, V.vsa_grid(21, 30, 52), 128, 0, 128, p, 328, p,
                                ctypes.cast(bad, ctypes.c_void_p), 2, 0.1, p, p, p, ws, None) == V.VSA_ERR_INVALID
+    # a head of 2^23 tokens x 128 channels is 2 GiB: beyond the 32-bit descriptor size, rejected before any launch
+    big = V.vsa_grid(128, 256, 256)
+    assert L.vsa_profile_heads(p, p, p, 1, 1, big, 128, 0, 128, p, 328, p, layp, 2, 0.1,
+                               p, p, p, 1 << 40, None) == V.VSA_ERR_INVALID
+    assert L.vsa_profile_heads_noalloc(p, p, p, 1, 1, big, 128, 0, 128, p, 328, p, layp, 2, 0.1,
+                                       p, p, None) == V.VSA_ERR_INVALID
 
 
 def test_check_block_list_host():
