@@ -81,6 +81,23 @@ def test_profile_candidate_counts_and_identical_candidates(P):
         assert np.array_equal(ge[..., 1], ge[..., 3])      # identical candidates, identical errors
 
 
+def test_profile_two_batch_entries():
+    """B = 2: every (b, h) pair profiled on the shared rows, against the oracle;
+    the second batch entry holds different inputs (a different seed)."""
+    grid, bs = (6, 10, 12), 64
+    announce("profile B=2")
+    w = WAN480.scaled(name="b2", T=grid[0], Hh=grid[1], W=grid[2], H=3, amplitude=2.0, seed=21, bs=bs)
+    q1, k1, v1 = make_qkv(w)
+    q2, k2, v2 = make_qkv(w.scaled(seed=22))
+    q, k, v = (np.concatenate(p, axis=0) for p in ((q1, q2), (k1, k2), (v1, v2)))
+    rows = np.sort(np.random.default_rng([21, 1]).choice(w.N, size=40, replace=False)).astype(np.int32)
+    cands = np.stack([OM.pattern_mask(grid, bs, "spatial", 0), OM.pattern_mask(grid, bs, "temporal", 3)])
+    err, ch = V.vsa_profile_heads(dev(q), dev(k), dev(v), grid, bs, dev_i32(rows), dev_u8(cands), [0, 1])
+    er, cr = OPR.profile_heads(q, k, v, grid, bs, rows, cands, [0, 1])
+    assert host(err).shape == (2, 3, 2)
+    check_profile(host(err), host(ch), er, cr, "B=2")
+
+
 @pytest.mark.parametrize("bs,shuffle", [(48, True), (64, True), (40, False)])
 def test_profile_ragged_blocks_and_unsorted_rows(bs, shuffle):
     """Blocks that are not a whole number of 32-key words (bit words built run
