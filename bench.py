@@ -723,23 +723,29 @@ def extra_layers(torch, V, PL, T, wan_dense, wan_attn_tflops):
     q, k, v = (torch.from_numpy(x).to(torch.bfloat16).to(dev) for x in make_qkv(w))
     n_cubes, k_max = PL.cube_budget(w.grid, w.extra["k_frac"])
     blk = V.vsa_cube_block_len(w.grid)
+    # every step writes into buffers allocated once, as a layer run step after step would
     st = {}
+    cube_buf = [V.vsa_permute(x, w.grid, V.VSA_PERM_CUBE4) for x in (q, k, v)]
+    s_buf = V.vsa_block_scores(cube_buf[0], cube_buf[1], 64, blk_len=blk)
+    sel_buf = V.vsa_select_topk(s_buf[0], k_max, w.extra["top_p"])
+    oc_buf, o_buf = torch.empty_like(cube_buf[0]), torch.empty_like(q)
 
     def cube_permute():
-        st["qc"], st["kc"], st["vc"] = (V.vsa_permute(x, w.grid, V.VSA_PERM_CUBE4) for x in (q, k, v))
+        st["qc"], st["kc"], st["vc"] = (V.vsa_permute(x, w.grid, V.VSA_PERM_CUBE4, out=b)
+                                        for x, b in zip((q, k, v), cube_buf))
 
     def cube_scores():
-        st["S"] = V.vsa_block_scores(st["qc"], st["kc"], 64, blk_len=blk)[0]
+        st["S"] = V.vsa_block_scores(st["qc"], st["kc"], 64, blk_len=blk, out=s_buf)[0]
 
     def cube_select():
-        st["idx"], st["cnt"] = V.vsa_select_topk(st["S"], k_max, w.extra["top_p"])
+        st["idx"], st["cnt"] = V.vsa_select_topk(st["S"], k_max, w.extra["top_p"], out=sel_buf)
 
     def cube_attn():
         st["oc"] = V.vsa_block_sparse_attn_fwd(st["qc"], st["kc"], st["vc"], 64, kv_idx=st["idx"], kv_cnt=st["cnt"],
-                                               blk_len=blk)
+                                               blk_len=blk, out=oc_buf)
 
     def cube_back():
-        st["o"] = V.vsa_permute(st["oc"], w.grid, V.VSA_PERM_CUBE4, inverse=True)
+        st["o"] = V.vsa_permute(st["oc"], w.grid, V.VSA_PERM_CUBE4, inverse=True, out=o_buf)
 
     ms, _ = queued(torch, T, [("a3_cube_permute_qkv", cube_permute), ("a4_block_scores", cube_scores),
                               ("a5_select_topk", cube_select), ("a7_attention", cube_attn),
@@ -747,6 +753,11 @@ def extra_layers(torch, V, PL, T, wan_dense, wan_attn_tflops):
     qc, kc, vc, S, idx, cnt, oc = (st[x] for x in ("qc", "kc", "vc", "S", "idx", "cnt", "oc"))
     fl = kept_flops_from_lists(idx, cnt, oc.shape[2], 64, 128, blk)
     t_att = ms["a7_attention"]
+    # the same attention launch alone, back to back on the layer's last lists
+    oc_alone = torch.empty_like(oc)
+    t_alone = T.per_call_ms(lambda: V.vsa_block_sparse_attn_fwd(qc, kc, vc, 64, kv_idx=idx, kv_cnt=cnt, blk_len=blk,
+                                                                out=oc_alone), 10)
+    del oc_alone
     nat_b = q.numel() * q.element_size()                         # one natural-order tensor
     cube_b = qc.numel() * qc.element_size()                      # one cube-major tensor, pad slots included
     gbs = {"a3_cube_permute_qkv": 3 * (nat_b + cube_b),          # read every token, write every slot
@@ -759,10 +770,12 @@ def extra_layers(torch, V, PL, T, wan_dense, wan_attn_tflops):
                                "k_max": k_max, "mean_kept": round(float(cnt.float().mean().item()), 2),
                                "kept_flops": fl, "attn_tflops": round(fl / (t_att * 1e-3) / 1e12, 2),
                                "pct_mfma_peak": round(100 * fl / (t_att * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+                               "a7_alone": {"ms": round(t_alone, 4), "tflops": round(fl / (t_alone * 1e-3) / 1e12, 2),
+                                            "what": "the layer's attention launch alone, 10 back to back"},
                                **speedups(wan_dense, t_att, sum(ms.values())),
                                "backward": time_backward(torch, V, T, qc, kc, vc, 64, fl, kv_idx=idx, kv_cnt=cnt,
                                                          blk_len=blk)}
-    del q, k, v, qc, kc, vc, oc, S, st
+    del q, k, v, qc, kc, vc, oc, S, st, cube_buf, s_buf, sel_buf, oc_buf, o_buf
     torch.cuda.empty_cache()
 
     w = LONG126
