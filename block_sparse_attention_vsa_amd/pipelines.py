@@ -90,10 +90,11 @@ def cube_layer(q, k, v, grid, k_frac, top_p, scale=None, stats=None):
     n_cubes, k_max = cube_budget(grid, k_frac)
     qc = vsa_permute(q, grid, VSA_PERM_CUBE4)
     kc = vsa_permute(k, grid, VSA_PERM_CUBE4)
-    vc = vsa_permute(v, grid, VSA_PERM_CUBE4)
     blk = vsa_cube_block_len(grid, device=q.device)
     S, _, _ = vsa_block_scores(qc, kc, 64, blk_len=blk, scale=scale)
     idx, cnt = vsa_select_topk(S, k_max, top_p)
+    # V is moved right before the attention reads it, so the last-level cache holds K and V then
+    vc = vsa_permute(v, grid, VSA_PERM_CUBE4)
     oc = vsa_block_sparse_attn_fwd(qc, kc, vc, 64, kv_idx=idx, kv_cnt=cnt, blk_len=blk, scale=scale)
     o = vsa_permute(oc, grid, VSA_PERM_CUBE4, inverse=True)
     if stats is not None:
