@@ -369,7 +369,7 @@ def main():
 
     extra = {}
     if not args.no_extra:
-        extra = extra_layers(torch, V, PL, T, dense, attn_tflops)
+        extra = extra_layers(torch, V, PL, T, dense, attn_tflops, kstats["warm"]["tflops_at_median"])
 
     digest = source_digest("attn_fwd.hip", "mfma_tile.h", "vsa_internal.h")
     # the chosen-candidate launch carries the frame-major loop whenever a
@@ -577,7 +577,7 @@ def speedups(dense, attn_ms, layer_ms):
             "speedup_vs_dense_pipeline": round(dense["best"] / layer_ms, 2)}
 
 
-def extra_layers(torch, V, PL, T, wan_dense, wan_attn_tflops):
+def extra_layers(torch, V, PL, T, wan_dense, wan_attn_tflops, wan_alone_tflops):
     """The other layers of the pages at their shapes, each step timed as device
     work (queued behind a lead spin, so no host latency is inside a bracket),
     with the dense baselines at the same shape for the speedups."""
@@ -611,10 +611,16 @@ def extra_layers(torch, V, PL, T, wan_dense, wan_attn_tflops):
     ms = {k_: round(v_, 4) for k_, v_ in ms.items()}
     fl = kept_flops_from_lists(idx, cnt, w.N, w.bs, 128)
     split_tflops = fl / (ms["chosen_attention"] * 1e-3) / 1e12
+    # the split's launch alone, timed as the all-spatial launch is in attention_launch_stats
+    # (one launch per lead spin, median): both then run at the clock a lone launch gets
+    alone = launch_stats(torch, T, lambda: V.vsa_block_sparse_attn_fwd_chosen(q, k, v, w.grid, w.bs, cand, [0, 1], ch,
+                                                                             out=o_c), fl, runs=20, warm=3)
     res["svg_6_6_split_wan480"] = {
         "ms": ms, "kept_flops": fl, "chosen_attn_tflops": round(split_tflops, 2),
         "fused_attn_tflops": round(fl / (ms["fused_attention"] * 1e-3) / 1e12, 2),
         "rate_vs_all_spatial_step_kernel": round(split_tflops / wan_attn_tflops, 3),
+        "chosen_alone": alone,
+        "rate_vs_all_spatial_alone": round(alone["warm"]["tflops_at_median"] / wan_alone_tflops, 3),
         "separate_total_ms": round(ms["separate_permute_qkv"] + ms["separate_attention"] + ms["separate_permute_o"], 4),
         "bit_identical": bool(torch.equal(o_c, o_f) and torch.equal(o_f, o_s)),
         **speedups(wan_dense, ms["chosen_attention"], ms["chosen_attention"])}
