@@ -22,6 +22,11 @@ ERR_REL = 1e-3      # error allowed on each candidate's profile error, relative 
 GAP_MIN = 1e-4      # choices must agree wherever the oracle's relative gap reaches this
 
 
+def bf16(x):
+    """fp32 array rounded to bf16 values (the inputs the GPU sees), as float64."""
+    return torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(torch.bfloat16).to(torch.float64).numpy()
+
+
 def check_profile(err_g, ch_g, err_r, ch_r, what):
     """A candidate's error is compared at the scale of the head's decision: the
     second-smallest oracle error e2 (a candidate with a larger error, at its own
@@ -79,6 +84,27 @@ def test_profile_candidate_counts_and_identical_candidates(P):
     check_profile(ge, host(ch), er, cr, f"P={P}")
     if P == 4:
         assert np.array_equal(ge[..., 1], ge[..., 3])      # identical candidates, identical errors
+
+
+def test_profile_large_logits_and_rows_a_candidate_keeps_nothing():
+    """Scores with a spread of about 35 (Q and K scaled by 6): the running offset
+    must keep every exp2 finite. One candidate keeps no key at all for one query
+    block, so its output there is 0 and its error is the dense output's square."""
+    grid, bs, H = (6, 10, 12), 64, 2
+    announce("profile large logits")
+    g = np.random.default_rng([31, 1])
+    N = grid[0] * grid[1] * grid[2]
+    q, k = (bf16((6.0 * g.standard_normal((1, H, N, 128))).astype(np.float32)) for _ in range(2))
+    v = bf16(g.standard_normal((1, H, N, 128)).astype(np.float32))
+    rows = np.sort(g.choice(N, size=48, replace=False)).astype(np.int32)
+    c0 = OM.pattern_mask(grid, bs, "spatial", 0)
+    qb = int(rows[5]) // bs
+    c0[qb, :] = 0                                           # the sampled row 5 keeps nothing under candidate 0
+    cands = np.stack([c0, OM.pattern_mask(grid, bs, "temporal", 2)])
+    err, ch = V.vsa_profile_heads(dev(q), dev(k), dev(v), grid, bs, dev_i32(rows), dev_u8(cands), [0, 1])
+    er, cr = OPR.profile_heads(q, k, v, grid, bs, rows, cands, [0, 1])
+    assert np.isfinite(host(err)).all()
+    check_profile(host(err), host(ch), er, cr, "large logits")
 
 
 def test_profile_two_batch_entries():
