@@ -44,30 +44,35 @@ def svg_masks(grid, bs, w_spatial, w_temporal, device="cuda"):
 
 def svg_layer(q, k, v, grid, bs, w_spatial, w_temporal, rows, scale=None, choice=None, cand=None, workspace=None,
               stats=None, fused=True):
-    """Returns (o, choice_host). `choice` [H] (host) skips the profiler; `rows`
-    (device int32) are the sampled query rows otherwise.
+    """Returns (o, choice_host). `choice` (host: [H], or [B][H]) skips the
+    profiler; `rows` (device int32) are the sampled query rows otherwise. The
+    host choice comes back as [H] for B = 1 and as [B][H] otherwise.
 
-    fused (default): the attention kernel reads each head's choice on the device,
-    compacts the chosen candidate's mask rows itself and applies the frame-major
-    order of temporal heads in its loads and stores; the host copy of the choice
-    is taken after the attention launch. fused=False: the same result, bit for
-    bit, through host choice -> mask -> list -> permute -> attention -> inverse
-    permute."""
+    fused (default): the attention kernel reads each (batch entry, head)'s choice
+    on the device, compacts the chosen candidate's mask rows itself and applies
+    the frame-major order of temporal heads in its loads and stores; the host
+    copy of the choice is taken after the attention launch. fused=False (B = 1
+    only): the same result, bit for bit, through host choice -> mask -> list ->
+    permute -> attention -> inverse permute."""
     import torch
     B, H = q.shape[:2]
-    if B != 1:
-        raise ValueError("svg_layer permutes heads by a per-head choice; call it per batch entry")
+    if B != 1 and not fused:
+        raise ValueError("the separate path permutes heads by a per-head choice; call it per batch entry")
     if cand is None:
         cand = svg_masks(grid, bs, w_spatial, w_temporal, q.device)
     if choice is None:
         _, ch = vsa_profile_heads(q, k, v, grid, bs, rows, cand, [0, 1], scale=scale, workspace=workspace)
     else:
-        ch = torch.tensor([[int(c) for c in choice]], dtype=torch.int32, device=q.device)
+        rows_c = [choice] if B == 1 and not isinstance(choice[0], (list, tuple)) else choice
+        ch = torch.tensor([[int(c) for c in r] for r in rows_c], dtype=torch.int32, device=q.device)
+        if tuple(ch.shape) != (B, H):
+            raise ValueError(f"choice must give one candidate per (batch entry, head): {B} x {H}")
     if fused:
         o = vsa_block_sparse_attn_fwd_chosen(q, k, v, grid, bs, cand, [0, 1], ch, scale=scale)
         if stats is not None:
             stats.update(cand=cand, choice=ch)
-        return o, [int(c) for c in ch[0].cpu().tolist()]
+        host_ch = [[int(c) for c in r] for r in ch.cpu().tolist()]
+        return o, host_ch[0] if B == 1 else host_ch
     sel = [int(c) for c in ch[0].cpu().tolist()]           # host decision: which heads move
     qm = vsa_permute(q, grid, VSA_PERM_FRAME_MAJOR, False, sel)
     km = vsa_permute(k, grid, VSA_PERM_FRAME_MAJOR, False, sel)

@@ -191,6 +191,28 @@ def test_svg_pipeline_wan_full_shape():
     assert_close_bf16(host(o2)[:, :, rows], ro2, "svg pipeline (profiled)")
 
 
+def test_svg_layer_two_batch_entries():
+    """The profiled layer with B = 2 (different inputs per entry): every (b, h)
+    gets its own choice on the device, the attention follows it, and the output
+    equals the oracle's layer under the same choices at every row."""
+    grid, bs, H = (4, 10, 12), 64, 3
+    announce("svg layer B=2")
+    w = WAN480.scaled(name="svg_b2", T=grid[0], Hh=grid[1], W=grid[2], H=H, amplitude=4.0, seed=41, bs=bs)
+    q1, k1, v1 = make_qkv(w)
+    q2, k2, v2 = make_qkv(w.scaled(seed=42))
+    q, k, v = (np.concatenate(p, axis=0) for p in ((q1, q2), (k1, k2), (v1, v2)))
+    rows = profile_rows(w)
+    o, ch = PL.svg_layer(dev(q), dev(k), dev(v), grid, bs, 0, 2, dev_i32(rows))
+    assert np.array(ch).shape == (2, H)
+    cands = np.stack([OM.pattern_mask(grid, bs, "spatial", 0), OM.pattern_mask(grid, bs, "temporal", 2)])
+    er, cr = OPR.profile_heads(q, k, v, grid, bs, rows, cands, [0, 1])
+    e = np.sort(er, axis=-1)
+    clear = (e[..., 1] - e[..., 0]) / np.maximum(e[..., 1], 1e-30) >= 2e-3
+    assert np.array_equal(np.array(ch)[clear], cr[clear])
+    ro, _ = OP.svg_pipeline(q, k, v, grid, bs, ch, 0, 2)
+    assert_close_bf16(host(o), ro, "svg layer B=2")
+
+
 def test_cube_pipeline_wan_full_shape():
     w = WAN480_CUBE
     announce("cube pipeline wan full")
