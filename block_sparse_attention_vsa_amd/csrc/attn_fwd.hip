@@ -253,7 +253,7 @@ __global__ __launch_bounds__(BS * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
     // walk 32-key sub-tiles, so that two stages still fit 4 workgroups per CU
     constexpr int D = 128, KT = (BS == 128) ? 64 : 32, NST = KT / 32, SUBB = KT * D * 2;
     constexpr int WAVES = BS / 32, THREADS = WAVES * 64, SUB = BS / KT;
-    constexpr float TAU = 8.f;
+    constexpr float TAU = 8.f, TAU_POW = 256.f;
     constexpr bool TWO_STAGES = true;
     __shared__ __attribute__((aligned(1024))) uint8_t k0[SUBB];
     __shared__ __attribute__((aligned(1024))) uint8_t v0[SUBB];
@@ -381,38 +381,52 @@ __global__ __launch_bounds__(BS * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
                     if (acc_key(st, x, half) >= vs) s[st][x] = -INFINITY;
         }
         // ---- online softmax with a lazily moved offset ---------------------------
-        float mx = -INFINITY;
-#pragma unroll
-        for (int st = 0; st < NST; ++st)
-#pragma unroll
-            for (int x = 0; x < 16; ++x) mx = fmaxf(mx, s[st][x]);
-        mx = pair_max(mx);
-        const float m_tile = mx * a.scale_log2;
-        const bool upd = m_tile > m_run + TAU;
-        const float m_new = upd ? m_tile : m_run;
-        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-        if (__ballot(upd)) {
-            const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);   // 1 where the offset stays
-            l_run *= alpha;
-#pragma unroll
-            for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-                for (int x = 0; x < 16; ++x) o_acc[dt][x] *= alpha;
-        }
-        m_run = m_new;
-        // p in fp32 feeds the row sum (so the log-sum-exp keeps fp32 accuracy);
-        // its bf16 rounding feeds the P V product
+        // p is first formed under the current offset. The offset only moves when
+        // the tile's maximum exceeds it by more than TAU (log2 units), i.e. when
+        // some p exceeds 2^TAU; a lane whose p sum to at most 2^TAU has none, so
+        // while every lane's sum stays there the row maximum is never needed.
+        // Otherwise the maximum is taken and p formed again where the offset
+        // moves. p in fp32 feeds the row sum (so the log-sum-exp keeps fp32
+        // accuracy); its bf16 rounding feeds the P V product.
         bf16x8 pf[NST][2];
-        float ps[4] = {0.f, 0.f, 0.f, 0.f};
+        float lsum;
+        auto probs = [&](float m_use) __attribute__((always_inline)) {
+            float ps[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int st = 0; st < NST; ++st)
+            for (int st = 0; st < NST; ++st)
 #pragma unroll
-            for (int x = 0; x < 16; ++x) {
-                const float p = __builtin_amdgcn_exp2f(fmaf(s[st][x], a.scale_log2, -m_use));
-                ps[x & 3] += p;
-                pf[st][x >> 3][x & 7] = (__bf16)p;
+                for (int x = 0; x < 16; ++x) {
+                    const float p = __builtin_amdgcn_exp2f(fmaf(s[st][x], a.scale_log2, -m_use));
+                    ps[x & 3] += p;
+                    pf[st][x >> 3][x & 7] = (__bf16)p;
+                }
+            lsum = (ps[0] + ps[1]) + (ps[2] + ps[3]);
+        };
+        probs(m_run == -INFINITY ? 0.f : m_run);
+        const bool stays = m_run != -INFINITY && lsum <= TAU_POW;
+        if (__ballot(!stays)) {
+            float mx = -INFINITY;
+#pragma unroll
+            for (int st = 0; st < NST; ++st)
+#pragma unroll
+                for (int x = 0; x < 16; ++x) mx = fmaxf(mx, s[st][x]);
+            mx = pair_max(mx);
+            const float m_tile = mx * a.scale_log2;
+            const bool upd = m_tile > m_run + TAU;
+            const float m_new = upd ? m_tile : m_run;
+            const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+            if (__ballot(upd)) {
+                const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);   // 1 where the offset stays
+                l_run *= alpha;
+#pragma unroll
+                for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+                    for (int x = 0; x < 16; ++x) o_acc[dt][x] *= alpha;
+                probs(m_use);
             }
-        l_run += (ps[0] + ps[1]) + (ps[2] + ps[3]);
+            m_run = m_new;
+        }
+        l_run += lsum;
         // ---- O^T += V^T P^T, V^T through transposing LDS reads -------------------
         sub_pv_ahead<NST>(o_acc, vt, pf, vfirst, vad);
     };

@@ -166,7 +166,7 @@ __device__ __forceinline__ int block_scan_256(int v, int* tmp, int& total) {
 
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void attn_varlen_kernel(VarArgs a) {
     constexpr int D = 128, KT = kVarKT, NST = KT / 32, SUBB = KT * D * 2, WAVES = 4, THREADS = 256;
-    constexpr float TAU = 8.f;
+    constexpr float TAU = 8.f, TAU_POW = 256.f;
     __shared__ __attribute__((aligned(1024))) uint8_t k0[SUBB];
     __shared__ __attribute__((aligned(1024))) uint8_t v0[SUBB];
     __shared__ __attribute__((aligned(1024))) uint8_t k1[SUBB];
@@ -310,36 +310,48 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
                 for (int x = 0; x < 16; ++x)
                     if (acc_key(st, x, half) >= vs) s[st][x] = -INFINITY;
         }
-        float mx = -INFINITY;
-#pragma unroll
-        for (int st = 0; st < NST; ++st)
-#pragma unroll
-            for (int x = 0; x < 16; ++x) mx = fmaxf(mx, s[st][x]);
-        mx = pair_max(mx);
-        const float m_tile = mx * a.scale_log2;
-        const bool upd = m_tile > m_run + TAU;
-        const float m_new = upd ? m_tile : m_run;
-        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-        if (__ballot(upd)) {
-            const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-            l_run *= alpha;
-#pragma unroll
-            for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-                for (int x = 0; x < 16; ++x) o_acc[dt][x] *= alpha;
-        }
-        m_run = m_new;
+        // p is formed first under the current offset, which only moves when some
+        // p exceeds 2^TAU: a lane whose p sum to at most 2^TAU has none, so the
+        // row maximum is taken only when some lane's sum passes 2^TAU
         bf16x8 pf[NST][2];
-        float ps[4] = {0.f, 0.f, 0.f, 0.f};
+        float lsum;
+        auto probs = [&](float m_use) __attribute__((always_inline)) {
+            float ps[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int st = 0; st < NST; ++st)
+            for (int st = 0; st < NST; ++st)
 #pragma unroll
-            for (int x = 0; x < 16; ++x) {
-                const float p = __builtin_amdgcn_exp2f(fmaf(s[st][x], a.scale_log2, -m_use));
-                ps[x & 3] += p;
-                pf[st][x >> 3][x & 7] = (__bf16)p;
+                for (int x = 0; x < 16; ++x) {
+                    const float p = __builtin_amdgcn_exp2f(fmaf(s[st][x], a.scale_log2, -m_use));
+                    ps[x & 3] += p;
+                    pf[st][x >> 3][x & 7] = (__bf16)p;
+                }
+            lsum = (ps[0] + ps[1]) + (ps[2] + ps[3]);
+        };
+        probs(m_run == -INFINITY ? 0.f : m_run);
+        const bool stays = m_run != -INFINITY && lsum <= TAU_POW;
+        if (__ballot(!stays)) {
+            float mx = -INFINITY;
+#pragma unroll
+            for (int st = 0; st < NST; ++st)
+#pragma unroll
+                for (int x = 0; x < 16; ++x) mx = fmaxf(mx, s[st][x]);
+            mx = pair_max(mx);
+            const float m_tile = mx * a.scale_log2;
+            const bool upd = m_tile > m_run + TAU;
+            const float m_new = upd ? m_tile : m_run;
+            const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+            if (__ballot(upd)) {
+                const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+                l_run *= alpha;
+#pragma unroll
+                for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+                    for (int x = 0; x < 16; ++x) o_acc[dt][x] *= alpha;
+                probs(m_use);
             }
-        l_run += (ps[0] + ps[1]) + (ps[2] + ps[3]);
+            m_run = m_new;
+        }
+        l_run += lsum;
         sub_pv_ahead<NST>(o_acc, vt, pf, vfirst, vad);
     };
 
