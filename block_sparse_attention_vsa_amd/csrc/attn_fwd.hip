@@ -31,6 +31,7 @@
 namespace vsa {
 
 constexpr int kMaxMaskBlocks = 4096;   // key blocks a mask row may hold (mask form)
+constexpr int64_t kLlcBytes = 256ll << 20;   // MI355X last-level (Infinity) cache
 
 struct AttnArgs {
     const uint16_t* q;
@@ -64,6 +65,9 @@ struct AttnArgs {
     // heads grouped by a host-known kind (frame-major or not) for the XCD deal;
     // all zero = no grouping
     uint64_t head_groups[kGroups];
+    // D = 128 bf16 kernel without grouping: 1 = deal runs of items (run_remap)
+    // instead of contiguous eighths (xcd_remap)
+    int32_t head_runs;
 };
 
 // Natural row of permuted row r (r < N) for a frame-major head.
@@ -271,7 +275,7 @@ __global__ __launch_bounds__(BS * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
     int item = a.head_choice ? chosen_item(a, blockIdx.x)
                              : ((a.head_groups[0] | a.head_groups[1])
                                     ? group_remap(blockIdx.x, a.num_items, a.nb, a.head_groups) : -1);
-    if (item < 0) item = xcd_remap(blockIdx.x, a.num_items);
+    if (item < 0) item = a.head_runs ? run_remap(blockIdx.x, a.num_items) : xcd_remap(blockIdx.x, a.num_items);
     const int bh = item / nqb, qb = item - bh * nqb;
     const int64_t head_off = (int64_t)bh * a.N * D;
     const int valid_q = block_valid_c(a.blk_len, qb, BS, a.N);
@@ -626,6 +630,13 @@ int prepare_attn(const char* fn, AttnArgs& a, const void* q, const void* k, cons
     a.num_items = (int32_t)items;
     a.scale_log2 = (float)((double)scale * 1.4426950408889634);
     a.T = 1; a.HW = N; a.div_T = FastDiv(1u);
+    // Every query block of a head streams that head's kept K and V blocks. Dealt
+    // in contiguous eighths, the 8 XCDs work on 8 different heads at once; when
+    // 8 heads' K and V exceed the 256 MB last-level cache, the blocks that miss
+    // L2 come from HBM, so runs of items are dealt instead and the XCDs share
+    // one or two heads' K and V in that cache. Below that size the eighths keep
+    // more of each XCD's neighbours in its L2.
+    a.head_runs = 8 * (2 * (int64_t)N * D * elt) > kLlcBytes;
     return VSA_OK;
 }
 

@@ -156,6 +156,19 @@ int vsa_selftest_host(void) {
                             return vsa::fail(VSA_ERR_INVALID, "group_remap: unequal share nb=%d heads=%d", nb, BH);
                 }
             }
+    // run_remap: a bijection on [0, G) around whole groups of 8 runs and ragged tails
+    const int gs[] = {1, 7, 8, 511, 512, 513, 1023, 1024, 1536, 12 * 1536, 24 * 929, 12 * 1536 + 37};
+    for (int G : gs) {
+        seen.assign(G, 0);
+        for (int bid = 0; bid < G; ++bid) {
+            const int it = vsa::run_remap(bid, G);
+            if (it < 0 || it >= G || seen[it]++)
+                return vsa::fail(VSA_ERR_INVALID, "run_remap: not a bijection G=%d", G);
+            // inside whole groups, XCD bid % 8 takes runs x, x + 8, ... in order
+            if (bid < G / (8 * vsa::kHeadRun) * (8 * vsa::kHeadRun) && (it / vsa::kHeadRun) % 8 != (bid & 7))
+                return vsa::fail(VSA_ERR_INVALID, "run_remap: run on the wrong XCD G=%d", G);
+        }
+    }
     return VSA_OK;
 }
 

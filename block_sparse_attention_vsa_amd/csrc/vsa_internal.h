@@ -65,6 +65,21 @@ __host__ __device__ __forceinline__ int xcd_remap(int bid, int G) {
     return x * q + (x < r ? x : r) + j;
 }
 
+// The same round-robin dispatch, with the items cut into runs of kHeadRun
+// consecutive items that are dealt to the XCDs in turn: XCD x takes runs x,
+// x + 8, x + 16, ..., a run's items in order. Each XCD still walks neighbouring
+// items (one run is as many workgroups as an XCD holds at once), but the 8 XCDs
+// now work on 8 neighbouring runs, i.e. on one or two heads at a time instead
+// of 8 far-apart heads. The items past the last whole group of 8 runs map to
+// themselves. A bijection on [0, G).
+constexpr int kHeadRun = 64;
+__host__ __device__ __forceinline__ int run_remap(int bid, int G) {
+    const int full = G / (8 * kHeadRun) * (8 * kHeadRun);
+    if (bid >= full) return bid;
+    const int x = bid & 7, j = bid >> 3;
+    return ((j / kHeadRun) * 8 + x) * kHeadRun + j % kHeadRun;
+}
+
 // Work items of heads that run different patterns, dealt evenly over the XCDs.
 // Items are (head, block) pairs, item = head * nb + block, G = heads * nb. Heads
 // are grouped (gm[g] has bit h set for each head h of group g, heads < 64,
