@@ -6,24 +6,33 @@
 // and query i, O_i = sum_j softmax_j(scale <q_i, k_j>) v_j over the valid keys j
 // of the key blocks kept for i's query block. Masked tiles are never loaded.
 //
-// bf16 kernel, one workgroup per (b, h, query block of BS rows), BS/32 waves:
-//  * each wave owns 32 query rows; Q stays in registers for the whole loop;
-//  * for every kept key block the workgroup stages K (row-major) and V
-//    (transposed, keys contiguous per channel) in LDS with XOR-swizzled 16-byte
-//    chunks, so every 8-lane group of a ds_read_b128 touches distinct banks;
+// bf16 kernels, one workgroup per (b, h, query block of BS rows), BS/32 waves,
+// each wave owning 32 query rows with Q in registers for the whole loop:
 //  * S^T = K Q^T on v_mfma_f32_32x32x16_bf16: the accumulator gives each lane one
-//    query and 16 keys per 32-key sub-tile, so a query's row max and row sum are
-//    lane-local except for one exchange between the two half-waves;
+//    query and 16 keys per 32-key sub-tile, so a query's row sum (and, when it
+//    is needed, its row max) is lane-local except for one exchange between the
+//    two half-waves;
 //  * online softmax in fp32 in the log2 domain (scale * log2 e folded into one
 //    FMA before v_exp_f32), P rounded to bf16;
 //  * O^T += V^T P^T on the same MFMA with P taken straight from the score
-//    registers: the transposed-V chunk order in LDS matches the order in which
-//    the accumulator holds the keys (bits 2 and 3 of the key index swapped).
-//  * The grid is remapped so that consecutive query blocks of a head run on the
-//    same XCD (workgroups are dealt round-robin over the 8 XCDs), which keeps
-//    the overlapping key windows of neighbouring query blocks in that XCD's L2;
-//    when heads read different chosen patterns, every XCD takes an equal share
-//    of each pattern's heads.
+//    registers.
+// D = 128 (the video shapes): K and V sub-tiles go from HBM straight into
+// double-buffered LDS stages by buffer-load-to-LDS copies (XOR-swizzled 16-byte
+// chunks), V stays row-major and its transposed operand is read with
+// ds_read_b64_tr_b16, whose key order matches the score accumulator's. The
+// running offset moves lazily (only when a tile's maximum exceeds it by more
+// than TAU), and P is formed first under the current offset: the tile maximum
+// is only taken when some lane's P sum past 2^TAU, i.e. when it may move. The
+// kernel also reads rows through the frame-major map and per-head candidate
+// choices (the fused permutation paths). D = 64: threads stage K and a
+// transposed V (keys contiguous per channel) in LDS, and the offset is the
+// exact running maximum.
+// Work items are dealt to the XCDs (workgroups go round-robin over the 8 XCDs)
+// so that consecutive query blocks of a head run on one XCD and share its L2;
+// when 8 heads' K and V outgrow the last-level cache, runs of items are dealt
+// instead so the XCDs work on one or two heads at a time; when heads read
+// different chosen patterns, every XCD takes an equal share of each pattern's
+// heads.
 #include <math.h>
 
 #include "mfma_tile.h"
