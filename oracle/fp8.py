@@ -13,8 +13,13 @@ no quantisation scheme; the plainest reading, used here:
   codes 0.
 * V: one scale per (b, h, channel) over all positions, same rule.
 * The attention is then plain block-sparse attention on the dequantised values
-  code * s (``oracle.attention``); what the kernel rounds beyond that (P to e4m3
-  before P V, fp32 sums) is covered by the test tolerance.
+  code * s (``oracle.attention``). ``attention_fp8_rounded_p`` adds the usual FP8
+  attention practice of rounding the probabilities to e4m3 before they multiply
+  V: with m_i the row's largest kept logit, P_ij = exp(s_ij - m_i), o_i =
+  sum_j e4m3(P_ij) v_j / sum_j P_ij and lse_i = m_i + log sum_j P_ij. A kernel
+  with a lazily moved offset forms the same P whenever its offset is the row
+  maximum (e.g. when the maximum lies in the first kept tile); fp32 sums are
+  covered by the test tolerance.
 * V is stored transposed in tiles of 64 keys: [B, H, ceil(N / 64), D, 64], key
   k = 32 st + 8 g + 4 h + e (st, h in {0, 1}; g, e in [0, 4)) of a tile at column
   32 h + 16 st + 4 g + e, keys past N zero. (This is the order in which the
@@ -131,3 +136,36 @@ def attention_fp8(q, k, v, mask, bs: int, blk_len=None, scale=None):
         scale = 1.0 / np.sqrt(np.asarray(q).shape[-1])
     o, lse = block_sparse_attention(qd, kd, vd, mask, bs, blk_len, scale)
     return o, lse, dict(q_codes=qc, q_scales=qs, k_codes=kc, k_scales=ks, v_codes=vc, v_scales=vs)
+
+
+def attention_fp8_rounded_p(q, k, v, mask, bs: int, scale=None, rows=None):
+    """(o, lse) of the natural blocked layout (position i in block i // bs, the
+    last block ragged): attention on the dequantised Q, K, V with the
+    probabilities rounded to e4m3 before they multiply V (module text); mask
+    [nqb, nkb] | [H, nqb, nkb] | [B, H, nqb, nkb]. Rows that keep nothing get
+    o = 0 and lse = -inf."""
+    qd = dequantise_rows(*quantise_rows(q))
+    kd = dequantise_rows(*quantise_rows(k))
+    vd = dequantise_channels(*quantise_channels(v))
+    B, H, N, D = qd.shape
+    scale = 1.0 / np.sqrt(D) if scale is None else float(scale)
+    m4 = np.asarray(mask)
+    m4 = np.broadcast_to(m4, (B, H) + m4.shape[-2:]) if m4.ndim < 4 else m4
+    rows = np.arange(N) if rows is None else np.asarray(rows, np.int64)
+    o = np.zeros((B, H, rows.size, D))
+    lse = np.full((B, H, rows.size), -np.inf)
+    for b in range(B):
+        for h in range(H):
+            for qb in np.unique(rows // bs):
+                sel = np.nonzero(rows // bs == qb)[0]
+                keys = np.concatenate([np.arange(kb * bs, min(N, (kb + 1) * bs))
+                                       for kb in np.nonzero(m4[b, h, qb])[0]] + [np.zeros(0, np.int64)])
+                if keys.size == 0:
+                    continue
+                s = scale * (qd[b, h, rows[sel]] @ kd[b, h, keys].T)
+                m = s.max(axis=1, keepdims=True)
+                pr = np.exp(s - m)
+                l = pr.sum(axis=1, keepdims=True)
+                o[b, h, sel] = (e4m3_decode(e4m3_encode(pr)) @ vd[b, h, keys]) / l
+                lse[b, h, sel] = (m + np.log(l))[:, 0]
+    return o, lse

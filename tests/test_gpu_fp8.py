@@ -1,7 +1,8 @@
 """GPU parity of the FP8 (e4m3) path against the oracle: the quantisers bit for
 bit (codes and scales), attention whose probabilities are exact in e4m3 (one or
 two equal maxima per row) to the bf16 output precision, random problems within
-the error that rounding P to e4m3 can cause, and sampled rows at the Wan shape."""
+the error that rounding P to e4m3 can cause, the rounded-P definition itself
+where the kernel's offset is the row maximum, and sampled rows at the Wan shape."""
 import numpy as np
 import pytest
 import torch
@@ -124,3 +125,41 @@ def test_fp8_attention_wan_shape_sampled():
     d = np.abs(go - ro)
     assert d.max() <= FP8_MAX_REL * np.abs(ro).max() and d.mean() <= FP8_MEAN_REL * np.abs(ro).mean()
     assert_lse_close(host(lse)[:, :, rows], rl, "fp8 wan", tol=2e-3)
+
+
+def test_fp8_attention_rounded_p_when_the_first_tile_holds_the_row_max():
+    """Key 0 carries every row's largest logit (its only nonzero channel meets a
+    constant channel of every query) and block 0 is kept by every query block, so
+    the kernel's first tile sets its running offset to the row maximum and it never
+    moves: the kernel then forms exactly the oracle's P = exp(s - max), rounded to
+    e4m3 before P V. Compared with that definition to the bf16 output precision
+    (a P at an e4m3 rounding midpoint may still round the other way in fp32)."""
+    announce("fp8 attention rounded P, max in the first tile")
+    g = np.random.default_rng(21)
+    B, H, N, D, bs = 1, 2, 1000, 128, 128
+    nb = -(-N // bs)
+    q, k, v = (g.standard_normal((B, H, N, D)) for _ in range(3))
+    q[..., 0] = 2.0
+    k[:, :, 0, :] = 0.0
+    k[:, :, 0, 0] = 31.0
+    q, k, v = (bf16_values(x) for x in (q, k, v))
+    mask = (g.random((B, H, nb, nb)) < 0.5).astype(np.uint8)
+    mask[..., 0] = 1
+    # precondition, on the dequantised values the kernel sees: key 0 is every row's maximum
+    qd = OF.dequantise_rows(*OF.quantise_rows(q))
+    kd = OF.dequantise_rows(*OF.quantise_rows(k))
+    s = np.einsum("bhnd,bhmd->bhnm", qd, kd)
+    kept = mask[:, :, np.arange(N)[:, None] // bs, np.arange(N)[None, :] // bs].astype(bool)
+    others = np.where(kept, s, -np.inf)
+    others[..., 0] = -np.inf
+    assert (s[..., 0] > others.max(axis=-1) + 1.0).all()
+    o, lse = V.vsa_block_sparse_attn_fwd_fp8(*quantised(q, k, v), bs, mask=dev_u8(mask), return_lse=True)
+    ro, rl = OF.attention_fp8_rounded_p(q, k, v, mask, bs)
+    go = host(o)
+    d = np.abs(go - ro)
+    print(f"fp8 rounded-P: max {d.max() / np.abs(ro).max():.3e} mean {d.mean() / np.abs(ro).mean():.3e} (relative)")
+    # measured 4.2e-3 / 1.4e-3 of the largest / mean magnitude; without the e4m3
+    # rounding of P the reference moves by 1.2e-2 on the mean, four times the bar
+    assert d.max() <= 1e-2 * np.abs(ro).max() and d.mean() <= 3e-3 * np.abs(ro).mean()
+    # the row sums take the unrounded P in fp32 (measured 4.4e-6)
+    assert_lse_close(host(lse), rl, "fp8 rounded P", tol=1e-4)

@@ -101,3 +101,67 @@ def test_attention_on_exactly_quantisable_inputs_equals_bf16_oracle():
     o, l = OA.block_sparse_attention(q, k, v, mask, 64, scale=scale)
     np.testing.assert_allclose(o8, o, rtol=1e-12, atol=1e-9)
     np.testing.assert_allclose(l8, l, rtol=1e-12)
+
+
+def _dequantised(q, k, v):
+    return (OF.dequantise_rows(*OF.quantise_rows(q)), OF.dequantise_rows(*OF.quantise_rows(k)),
+            OF.dequantise_channels(*OF.quantise_channels(v)))
+
+
+def test_rounded_p_against_torch_cast_of_the_oracle_probabilities():
+    """The rounded-P attention recomputed another way: the plain oracle's
+    normalised probabilities p over the dequantised inputs, scaled so that the
+    row's largest is 1 (P = p / max p, whose sum is 1 / max p), rounded by torch's
+    float8_e4m3fn cast, times V, divided by that sum."""
+    g = np.random.default_rng(11)
+    B, H, N, D, bs = 1, 2, 150, 16, 32
+    q, k, v = (g.standard_normal((B, H, N, D)) * 2.0 for _ in range(3))
+    mask = (g.random((H, 5, 5)) < 0.6).astype(np.uint8)
+    mask[0, 2] = 0                                          # a query block that keeps nothing
+    o, lse = OF.attention_fp8_rounded_p(q, k, v, mask, bs)
+    qd, kd, vd = _dequantised(q, k, v)
+    _, l_ref, p = OA.block_sparse_attention(qd, kd, vd, mask, bs, return_probs=True)
+    pmax = p.max(axis=-1, keepdims=True)
+    ok = pmax > 0
+    P = np.where(ok, p / np.where(ok, pmax, 1.0), 0.0)
+    Pr = torch.tensor(P).to(torch.float8_e4m3fn).to(torch.float64).numpy()
+    ref = np.einsum("bhij,bhjd->bhid", Pr, vd) * pmax
+    np.testing.assert_allclose(o, ref, rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(lse, l_ref, rtol=1e-12)
+    assert (o[0, 0, 64:96] == 0).all() and np.isneginf(lse[0, 0, 64:96]).all()
+
+
+def test_rounded_p_leaves_probabilities_on_the_e4m3_grid_unchanged():
+    """Logits ln 2 * n with n a power of two (or 0) up to 8: every P = 2^(n - 8) is
+    an e4m3 value (2^-8 a subnormal), so rounding changes nothing and the result is
+    the unrounded FP8 oracle's."""
+    g = np.random.default_rng(12)
+    B, H, N, D = 1, 1, 128, 4
+    q = np.zeros((B, H, N, D)); q[..., 0] = 1.0
+    k = np.zeros((B, H, N, D)); k[..., 0] = g.choice([0.0, 1.0, 2.0, 4.0, 8.0], N)
+    k[:, :, ::64, 0] = 8.0                                  # every 64-row block's amax is 8
+    v = g.standard_normal((B, H, N, D))
+    mask = np.ones((2, 2), np.uint8)
+    o, lse = OF.attention_fp8_rounded_p(q, k, v, mask, 64, scale=np.log(2.0))
+    o_u, lse_u, _ = OF.attention_fp8(q, k, v, mask, 64, scale=np.log(2.0))
+    np.testing.assert_allclose(o, o_u, rtol=1e-6, atol=1e-9)
+    np.testing.assert_allclose(lse, lse_u, rtol=1e-12)
+
+
+def test_rounded_p_within_half_a_step_of_the_unrounded_result():
+    """|o_rounded - o| <= sum_j |e4m3(P_j) - P_j| |v_j| / sum_j P_j, with the
+    rounding of each P at most half a step: 2^-4 P for normals (P >= 2^-6) and
+    2^-10 below; and the rounding does change the result on random inputs."""
+    g = np.random.default_rng(13)
+    B, H, N, D, bs = 1, 1, 96, 8, 32
+    q, k, v = (g.standard_normal((B, H, N, D)) * 1.5 for _ in range(3))
+    mask = np.ones((3, 3), np.uint8)
+    o, _ = OF.attention_fp8_rounded_p(q, k, v, mask, bs)
+    o_u, _, _ = OF.attention_fp8(q, k, v, mask, bs)
+    qd, kd, vd = _dequantised(q, k, v)
+    s = (qd[0, 0] @ kd[0, 0].T) / np.sqrt(D)
+    P = np.exp(s - s.max(axis=1, keepdims=True))
+    half = np.maximum(P * 2.0 ** -4, 2.0 ** -10)
+    bound = (half @ np.abs(vd[0, 0])) / P.sum(axis=1, keepdims=True)
+    assert (np.abs(o[0, 0] - o_u[0, 0]) <= bound * (1 + 1e-9)).all()
+    assert np.abs(o - o_u).max() > 1e-4
