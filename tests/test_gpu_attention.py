@@ -61,6 +61,29 @@ def test_bf16_random_masks_ragged_full_oracle(N, bs, D, H):
     assert torch.equal(o, o3)
 
 
+
+# Per-element bound from the kernel's roundings: P is rounded to bf16 (8
+# significant bits: relative error at most 2^-8) before P V and O once to bf16
+# (2^-8 of |O|); the fp32 scores, sums and exponentials add under 2e-4 relative
+# at these sizes. With p the exact normalised probabilities:
+# |O_kernel - O| <= (2^-8 + 2e-4) (sum_j p_j |v_j| + |O|).
+@pytest.mark.parametrize("N,bs,amp", [(1000, 128, 1.0), (777, 64, 1.0), (1000, 128, 3.0)])
+def test_bf16_attention_within_its_rounding_bound(N, bs, amp):
+    announce(f"attn bf16 rounding bound N={N} bs={bs} amp={amp}")
+    rng = np.random.default_rng(N + bs + 7)
+    H, D = 2, 128
+    q, k, v = (rng.standard_normal((1, H, N, D)).astype(np.float32) * a for a in (amp, amp, 1.0))
+    qd, kd, vd = dev(q), dev(k), dev(v)
+    q, k, v = host(qd), host(kd), host(vd)
+    mask = rand_mask(H, -(-N // bs), 0.4, N + 1)
+    o = V.vsa_block_sparse_attn_fwd(qd, kd, vd, bs, mask=dev_u8(mask))
+    ro, _, p = OA.block_sparse_attention(q, k, v, mask, bs, return_probs=True)
+    bound = (2.0 ** -8 + 2e-4) * (np.einsum("bhij,bhjd->bhid", p, np.abs(v)) + np.abs(ro))
+    d = np.abs(host(o) - ro)
+    print(f"bf16 rounding bound N={N} bs={bs} amp={amp}: worst |d| / bound {(d / bound).max():.3f}, "
+          f"max |d| {d.max():.3e}, mean |d| / mean |O| {d.mean() / np.abs(ro).mean():.3e}")
+    assert (d <= bound).all()
+
 def test_empty_rows_and_scaled_logits():
     announce("attn bf16 empty rows / large logits")
     N, bs, D, H = 512, 128, 128, 2
