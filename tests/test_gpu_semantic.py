@@ -230,10 +230,14 @@ def test_varlen_attention_ragged_clusters_full_oracle(seed):
     mask[0, 0, 6, :] = 0                                    # query cluster 6 keeps nothing
     qd, kd, vd = dev(q), dev(k), dev(v)
     o, lse = V.vsa_varlen_sparse_attn_fwd(qd, kd, vd, dev_i32(qo), dev_i32(ko), mask=dev_u8(mask), return_lse=True)
-    ro, rl = OA.masked_attention(q, k, v, mask, qblk, kblk)
+    ro, rl, p = OA.masked_attention(q, k, v, mask, qblk, kblk, return_probs=True)
     go, gl = host(o), host(lse)
     assert_close_bf16(go, ro, f"varlen seed={seed}")
     assert_lse_close(gl, rl, f"varlen seed={seed}")
+    # every element within the bound of its two bf16 roundings (P before P V, O
+    # once; 2^-8 each) plus 2e-4 for the fp32 arithmetic
+    bound = (2.0 ** -8 + 2e-4) * (np.einsum("bhij,bhjd->bhid", p, np.abs(v)) + np.abs(ro))
+    assert (np.abs(go - ro) <= bound).all(), f"varlen seed={seed}: past the rounding bound"
     rows6 = slice(qo[0, 0, 6], qo[0, 0, 7])
     assert (go[0, 0, rows6] == 0).all() and np.isneginf(gl[0, 0, rows6]).all()
     idx, cnt = OM.mask_to_list(mask)
