@@ -84,6 +84,35 @@ def test_bf16_attention_within_its_rounding_bound(N, bs, amp):
           f"max |d| {d.max():.3e}, mean |d| / mean |O| {d.mean() / np.abs(ro).mean():.3e}")
     assert (d <= bound).all()
 
+
+@pytest.mark.parametrize("slope", [10.0, 3.0, -6.0])
+def test_offset_paths_with_scores_rising_or_falling_along_the_keys(slope):
+    """Every query's score moves by `slope` log2 units per 64 keys (plus a little
+    noise), so the kernel's running offset has to move on every sub-tile (10), the
+    lanes' p sums pass 2^8 while the offset may stay (3), or the first sub-tile
+    holds the row maximum and the offset never moves (-6). Each element within the
+    bound of its two bf16 roundings; LSE to the oracle."""
+    announce(f"attn bf16 offset paths slope={slope}")
+    rng = np.random.default_rng(31)
+    N, bs, D, H = 500, 128, 128, 2
+    scale = 1.0 / np.sqrt(D)
+    per_key = slope / 64 / (scale * np.log2(np.e))       # channel-0 step of k per key
+    q = (0.05 * rng.standard_normal((1, H, N, D))).astype(np.float32)
+    k = (0.05 * rng.standard_normal((1, H, N, D))).astype(np.float32)
+    v = rng.standard_normal((1, H, N, D)).astype(np.float32)
+    q[..., 0] = 1.0
+    k[..., 0] = per_key * (np.arange(N) - (N - 1 if slope > 0 else 0))
+    qd, kd, vd = dev(q), dev(k), dev(v)
+    q, k, v = host(qd), host(kd), host(vd)
+    mask = np.ones((1, H, 4, 4), np.uint8)
+    o, lse = V.vsa_block_sparse_attn_fwd(qd, kd, vd, bs, mask=dev_u8(mask), return_lse=True)
+    ro, rl, p = OA.block_sparse_attention(q, k, v, mask, bs, return_probs=True)
+    bound = (2.0 ** -8 + 2e-4) * (np.einsum("bhij,bhjd->bhid", p, np.abs(v)) + np.abs(ro))
+    d = np.abs(host(o) - ro)
+    print(f"offset paths slope={slope}: worst |d| / bound {(d / bound).max():.3f}")
+    assert (d <= bound).all()
+    assert_lse_close(host(lse), rl, f"offset paths slope={slope}")
+
 def test_empty_rows_and_scaled_logits():
     announce("attn bf16 empty rows / large logits")
     N, bs, D, H = 512, 128, 128, 2
