@@ -247,6 +247,33 @@ def test_varlen_attention_ragged_clusters_full_oracle(seed):
     assert torch.equal(o, o3)
 
 
+
+@pytest.mark.parametrize("slope", [10.0, 3.0, -6.0])
+def test_varlen_offset_paths_with_scores_rising_or_falling(slope):
+    """As for the block kernel: scores moving by `slope` log2 units per 64 keys
+    along the kept key clusters drive the running offset through every path."""
+    announce(f"varlen offset paths slope={slope}")
+    rng = np.random.default_rng(32)
+    sizes_q, sizes_k = np.array([260, 240]), np.array([100, 150, 250])
+    N, D = 500, 128
+    scale = 1.0 / np.sqrt(D)
+    per_key = slope / 64 / (scale * np.log2(np.e))
+    q = bf16(0.05 * rng.standard_normal((1, 1, N, D)))
+    k = 0.05 * rng.standard_normal((1, 1, N, D))
+    q[..., 0] = 1.0
+    k[..., 0] = per_key * (np.arange(N) - (N - 1 if slope > 0 else 0))
+    k = bf16(k)
+    v = rand_bf16((1, 1, N, D), 33)
+    mask = np.ones((1, 1, 2, 3), np.uint8)
+    qo, ko = offsets_of(sizes_q)[None, None], offsets_of(sizes_k)[None, None]
+    o, lse = V.vsa_varlen_sparse_attn_fwd(dev(q), dev(k), dev(v), dev_i32(qo), dev_i32(ko), mask=dev_u8(mask),
+                                          return_lse=True)
+    qblk, kblk = np.repeat(np.arange(2), sizes_q), np.repeat(np.arange(3), sizes_k)
+    ro, rl, p = OA.masked_attention(q, k, v, mask, qblk, kblk, return_probs=True)
+    bound = (2.0 ** -8 + 2e-4) * (np.einsum("bhij,bhjd->bhid", p, np.abs(v)) + np.abs(ro))
+    assert (np.abs(host(o) - ro) <= bound).all(), f"varlen slope={slope}: past the rounding bound"
+    assert_lse_close(host(lse), rl, f"varlen offset paths slope={slope}")
+
 def test_varlen_attention_unsorted_lists_and_all_kept():
     announce("varlen attn unsorted / dense")
     sizes = np.array([70, 130, 1, 250, 60, 9])
