@@ -32,6 +32,7 @@
 
 #include <algorithm>
 #include <mutex>
+#include <vector>
 
 #include "mfma_tile.h"
 
@@ -78,7 +79,7 @@ struct BitsArgs {
     uint32_t* bits;
     int32_t R, N, nb, bs, words, P, T, HW;
     int32_t layout[kProfMaxP];
-    FastDiv div_HW, div_bs;
+    FastDiv div_HW, div_bs, div_T;
 };
 
 __device__ __forceinline__ uint32_t layout_pos(const BitsArgs& a, int lay, uint32_t n) {
@@ -89,6 +90,38 @@ __device__ __forceinline__ uint32_t layout_pos(const BitsArgs& a, int lay, uint3
 
 // One thread per 32-key word; the 32 key positions are computed independently
 // (fully unrolled), so the 32 mask-byte loads are in flight together.
+// Keep bits of one 32-key word of a row under a mask stated in frame-major
+// order: key n = t * HW + s (natural order) sits at frame-major position
+// s * T + t, in block (s * T + t) / bs; bit b is set when key 32 wi + b is below
+// N and its block is kept in mrow. Consecutive keys of one frame step that
+// position by T, so they come in runs of about bs / T keys per block, and the
+// word is built run by run: one mask read and two divisions per run instead of
+// per key.
+__host__ __device__ inline uint32_t fm_word_bits(const uint8_t* mrow, uint32_t wi, uint32_t N, uint32_t T,
+                                                 uint32_t HW, uint32_t bs, const FastDiv& div_HW,
+                                                 const FastDiv& div_bs, const FastDiv& div_T) {
+    const uint32_t n0 = 32u * wi;
+    const uint32_t nend = N - n0 > 32u ? n0 + 32u : N;
+    if (n0 >= N) return 0u;
+    uint32_t word = 0u, n = n0;
+    uint32_t t = div_HW.div(n), sp = n - t * HW;
+    while (n < nend) {
+        const uint32_t seg_end = nend - n < HW - sp ? nend : n + (HW - sp);   // rest of frame t
+        while (n < seg_end) {
+            const uint32_t pos = sp * T + t;
+            const uint32_t blk = div_bs.div(pos);
+            const uint32_t run = div_T.div((blk + 1u) * bs - pos + T - 1u);    // keys left in block blk
+            const uint32_t end = seg_end - n < run ? seg_end : n + run;
+            if (mrow[blk]) word |= (uint32_t)(((1ull << (end - n0)) - 1ull) ^ ((1ull << (n - n0)) - 1ull));
+            sp += end - n;
+            n = end;
+        }
+        ++t;
+        sp = 0u;
+    }
+    return word;
+}
+
 __global__ __launch_bounds__(256) void prof_bits_kernel(BitsArgs a) {
     const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
     const int64_t total = (int64_t)a.P * a.R * a.words;
@@ -112,21 +145,8 @@ __global__ __launch_bounds__(256) void prof_bits_kernel(BitsArgs a) {
             for (int b = 0; b < 32; ++b)
                 if (32 * wi + b < a.N && mrow[a.div_bs.div((uint32_t)(32 * wi + b))]) word |= 1u << b;
         } else {
-            // frame-major: (t, s) of the word's first key, then stepped key by key
-            // (one division per word instead of one per key)
-            const uint32_t n0 = 32u * (uint32_t)wi;
-            uint32_t t = a.div_HW.div(n0), sp = n0 - t * (uint32_t)a.HW;
-#pragma unroll
-            for (int b = 0; b < 32; ++b) {
-                const bool in = 32 * wi + b < a.N;
-                const uint32_t pos = in ? sp * (uint32_t)a.T + t : 0u;       // dropped past N
-                const uint8_t m = mrow[a.div_bs.div(pos)];
-                if (m && in) word |= 1u << b;
-                if (++sp == (uint32_t)a.HW) {
-                    sp = 0;
-                    ++t;
-                }
-            }
+            word = fm_word_bits(mrow, (uint32_t)wi, (uint32_t)a.N, (uint32_t)a.T, (uint32_t)a.HW, (uint32_t)a.bs,
+                                a.div_HW, a.div_bs, a.div_T);
         }
     }
     a.bits[e] = word;
@@ -585,6 +605,7 @@ int profile_launch(const void* q, const void* k, const void* v, int B, int H, vs
     for (int p = 0; p < kProfMaxP; ++p) ba.layout[p] = p < P ? cand_layout[p] : 0;
     ba.div_HW = FastDiv((uint32_t)ba.HW);
     ba.div_bs = FastDiv((uint32_t)bs);
+    ba.div_T = FastDiv((uint32_t)ba.T);
     int64_t nbits = (int64_t)P * R * pl.words;
     hipLaunchKernelGGL(prof_bits_kernel, dim3((unsigned)((nbits + 255) / 256)), dim3(256), 0, s, ba);
     int st = launch_status("vsa_profile_heads (bits)");
@@ -691,3 +712,37 @@ extern "C" int vsa_profile_heads_noalloc(const void* q, const void* k, const voi
     return profile_launch(q, k, v, B, H, g, D, bs, rows, R, cand_masks, cand_layout, P, scale, err, choice, pl, ws,
                           as_stream(stream));
 }
+
+namespace vsa {
+
+// Host check of fm_word_bits: every word of rows under random masks, against the
+// key-by-key rule, on the video grids and small ragged ones.
+int profile_selftest_host() {
+    const uint32_t shapes[][3] = {{21, 1560, 128}, {33, 3600, 128}, {126, 1560, 128}, {3, 5, 4}, {4, 30, 64},
+                                  {7, 9, 8}, {1, 100, 64}, {5, 1, 4}, {2, 33, 64}, {9, 7, 128}};
+    uint32_t lcg = 12345u;
+    for (const auto& sh : shapes) {
+        const uint32_t T = sh[0], HW = sh[1], bs = sh[2], N = T * HW, nb = (N + bs - 1) / bs;
+        const FastDiv dH(HW), dB(bs), dT(T);
+        std::vector<uint8_t> mrow(nb);
+        for (int rep = 0; rep < 2; ++rep) {
+            for (auto& m : mrow) {
+                lcg = lcg * 1664525u + 1013904223u;
+                m = (lcg >> 24) % 5 < 2;
+            }
+            for (uint32_t wi = 0; 32 * wi < N; ++wi) {
+                uint32_t ref = 0;
+                for (uint32_t b = 0; b < 32 && 32 * wi + b < N; ++b) {
+                    const uint32_t n = 32 * wi + b, t = n / HW, sp = n % HW;
+                    if (mrow[(sp * T + t) / bs]) ref |= 1u << b;
+                }
+                if (fm_word_bits(mrow.data(), wi, N, T, HW, bs, dH, dB, dT) != ref)
+                    return fail(VSA_ERR_INVALID, "fm_word_bits wrong at T=%u HW=%u bs=%u word %u", T, HW, bs, wi);
+            }
+        }
+    }
+    return VSA_OK;
+}
+
+}  // namespace vsa
+

@@ -107,6 +107,8 @@ int vsa_selftest_host(void) {
     }
     const int pst = vsa::permute_selftest_host();
     if (pst != VSA_OK) return pst;
+    const int bst = vsa::profile_selftest_host();
+    if (bst != VSA_OK) return bst;
     // group_remap: a bijection on [0, G) (or -1 everywhere) for head counts,
     // block counts and group patterns around the video shapes; with one group it
     // is xcd_remap, and every XCD gets an equal share (+-1 item) of each group

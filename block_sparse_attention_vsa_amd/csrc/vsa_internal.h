@@ -15,6 +15,7 @@ namespace vsa {
 int fail(int status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
 int launch_status(const char* what);   // VSA_OK or VSA_ERR_LAUNCH after a launch
 int permute_selftest_host();           // host check of the layout maps (permute.hip)
+int profile_selftest_host();           // host check of the frame-major keep bits (profile.hip)
 
 inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
