@@ -179,3 +179,25 @@ def test_full_shape_spatial_masks_sampled_rows(w, H):
     ro, rl = OA.block_sparse_attention(q, k, v, mask, w.bs, rows=rows)
     assert_close_bf16(go, ro, w.name)
     assert_lse_close(gl, rl, w.name)
+
+
+@pytest.mark.parametrize("w,H", [(HUNYUAN720, 3), (LONG126, 2)])
+def test_every_tile_kept_at_the_large_shapes_sampled_rows(w, H):
+    """The dense baselines the speedups are quoted against: every tile kept at the
+    HunyuanVideo and long-horizon shapes, where 8 heads' K and V outgrow the
+    last-level cache and work items are dealt to the XCDs in runs; sampled rows
+    (first and last row of every 16th block and of the last block, plus seeded
+    rows) against dense attention."""
+    announce(f"attn bf16 every tile kept {w.name} H={H}")
+    qd, kd, vd = (dev(x) for x in make_qkv(w, H=H))
+    q, k, v = host(qd), host(kd), host(vd)                   # the exact bf16 values the GPU sees
+    nb = w.nb
+    mask = np.ones((1, H, nb, nb), np.uint8)
+    o, lse = V.vsa_block_sparse_attn_fwd(qd, kd, vd, w.bs, mask=dev_u8(mask), return_lse=True)
+    blocks = np.r_[np.arange(0, nb, 16), nb - 1]
+    rows = np.unique(np.concatenate([blocks * w.bs, np.minimum(blocks * w.bs + w.bs, w.N) - 1,
+                                     np.random.default_rng(w.seed).choice(w.N, 256, replace=False)]))
+    ro, rl = OA.dense_attention(q, k, v, rows=rows)
+    assert_close_bf16(host(o)[:, :, rows], ro, f"{w.name} every tile kept")
+    assert_lse_close(host(lse)[:, :, rows], rl, f"{w.name} every tile kept")
+
