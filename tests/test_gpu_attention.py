@@ -181,11 +181,11 @@ def test_full_shape_spatial_masks_sampled_rows(w, H):
     assert_lse_close(gl, rl, w.name)
 
 
-@pytest.mark.parametrize("w,H", [(HUNYUAN720, 3), (LONG126, 2)])
+@pytest.mark.parametrize("w,H", [(WAN480, 2), (HUNYUAN720, 3), (LONG126, 2)])
 def test_every_tile_kept_at_the_large_shapes_sampled_rows(w, H):
     """The dense baselines the speedups are quoted against: every tile kept at the
-    HunyuanVideo and long-horizon shapes, where 8 heads' K and V outgrow the
-    last-level cache and work items are dealt to the XCDs in runs; sampled rows
+    Wan, HunyuanVideo and long-horizon shapes (at the last two, 8 heads' K and V
+    outgrow the last-level cache and work items are dealt to the XCDs in runs); sampled rows
     (first and last row of every 16th block and of the last block, plus seeded
     rows) against dense attention."""
     announce(f"attn bf16 every tile kept {w.name} H={H}")
